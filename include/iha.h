@@ -1,0 +1,147 @@
+/*
+ * iha.h - C ABI of the MI355X (gfx950) library for the forward pass of
+ * Interleaved Head Attention (IHA).
+ *
+ * What is computed: Algorithm 1 of the "Interleaved Head Attention" page
+ * (section 4; arXiv 2602.21371), for one layer and a batch of sequences:
+ *   pseudo-head mixing   Q~_{h,j} = sum_m alpha^Q_{m,h,j} X W_Q^(m)   (same for K, V)
+ *   pseudo-major stacking of the P pseudo-tokens of every token into P*N rows
+ *   per-head attention   softmax(Q-bar_h K-bar_h^T / sqrt(d)) V-bar_h  over those rows
+ *   collapse             O_h[t] = sum_{h'} sum_j R_{h,(h'-1)P+j} P_{h',j}[t]
+ *   concatenation        X~ = [O_1, ..., O_H]
+ * Attention follows the textbook chapter "Attention mechanism"
+ * (faketrader.github.io/llm-from-scratch/22-attention.html): scaled dot product
+ * (eq. 5.3), softmax restricted to each query's allowed set (eq. 5.11), and an
+ * explicit error instead of a NaN for a valid query whose allowed set is empty
+ * (section 5.3, "fully masked rows").  Biases are omitted (section 5.1), as in
+ * Algorithm 1.
+ *
+ * Stacked order and masks.  The pseudo-tokens of token t are interleaved
+ * (figure 1 of the IHA page): pseudo-token (t, j) has stacked position
+ * i = t*P + j (0-based).  The mask modes are defined on i:
+ *   IHA_MASK_NONE    every key is visible (Algorithm 1 as printed);
+ *   IHA_MASK_CAUSAL  key i' is visible from query i iff i' <= i;
+ *   IHA_MASK_WINDOW  key i' is visible iff i - window < i' <= i, with `window`
+ *                    counted in stacked positions (the page's sliding window
+ *                    of N/(2P); appendix C).  window < 1 leaves every row empty
+ *                    and is rejected with IHA_ERR_EMPTY_ROW.
+ *
+ * Layouts (row-major, contiguous, 0-based):
+ *   X        [B][N][D]          dtype IHA_BF16 or IHA_F32
+ *   W_Q/K/V  [D][H*d]           same dtype as X; head m's projection W^(m) is
+ *                               columns [m*d, (m+1)*d), d = D/H (section 3.1)
+ *   alpha_*  [H][H][P] float    alpha[m][h][j]; m = source head summed over,
+ *                               h = target head, j = pseudo index
+ *   R        [H][H*P]  float    column h'*P + j (0-based form of (h'-1)P + j)
+ *   X_out    [B][N][D] float    head h in columns [h*d, (h+1)*d)
+ *
+ * Precision.  IHA_F32: every step in fp32.  IHA_BF16: the mixing is folded
+ * into the weights in fp32, the folded weights, the projected Q/K/V and the
+ * attention probabilities are stored as fp16 for the matrix cores (fp32
+ * accumulation), softmax state and the per-head attention output are fp32,
+ * and X_out is fp32.
+ *
+ * Ownership and streams.  The caller owns every buffer; all device pointers
+ * must be on the current HIP device.  The library keeps no state between
+ * calls and allocates nothing: intermediate tensors live in the caller's
+ * workspace.  Work is enqueued on `stream` and the call returns without
+ * waiting, unless IHA_FLAG_CHECK is set.  Concurrent calls must not share a
+ * workspace.
+ *
+ * Errors.  Argument problems are detected on the host before anything is
+ * enqueued; X_out is then left untouched.  HIP launch failures give
+ * IHA_ERR_DEVICE.  With IHA_FLAG_CHECK the call synchronises `stream` and
+ * reports device-detected problems: a non-finite output (a non-finite input,
+ * or a value beyond the fp16 range in the IHA_BF16 path) as IHA_ERR_NONFINITE,
+ * and an empty allowed set as IHA_ERR_EMPTY_ROW.
+ */
+#ifndef IHA_H
+#define IHA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  IHA_OK = 0,
+  IHA_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, unknown enum */
+  IHA_ERR_SHAPE = 2,        /* D not a multiple of H, or a size beyond the supported range */
+  IHA_ERR_EMPTY_ROW = 3,    /* some valid query has no visible key */
+  IHA_ERR_NONFINITE = 4,    /* IHA_FLAG_CHECK: a non-finite value reached the output */
+  IHA_ERR_WORKSPACE = 5,    /* workspace missing or smaller than iha_workspace_bytes() */
+  IHA_ERR_UNSUPPORTED = 6,  /* head width d (or H) not compiled for this dtype */
+  IHA_ERR_DEVICE = 7        /* a HIP call failed */
+} iha_status;
+
+typedef enum { IHA_MASK_NONE = 0, IHA_MASK_CAUSAL = 1, IHA_MASK_WINDOW = 2 } iha_mask_mode;
+typedef enum { IHA_F32 = 0, IHA_BF16 = 1 } iha_dtype;
+
+/* Synchronise and report device-detected problems (see "Errors"). */
+#define IHA_FLAG_CHECK 1u
+
+typedef struct {
+  int64_t B;       /* batch size, >= 1 */
+  int64_t N;       /* tokens per sequence, >= 1 */
+  int64_t D;       /* model width, multiple of H */
+  int64_t H;       /* heads, 1..64 */
+  int64_t P;       /* pseudo-heads per head, >= 1 */
+  int64_t window;  /* IHA_MASK_WINDOW only: window in stacked positions, >= 1 */
+  int32_t mask;    /* iha_mask_mode */
+  int32_t dtype;   /* iha_dtype of X and W_* */
+  uint32_t flags;  /* IHA_FLAG_* */
+  uint32_t reserved; /* must be 0 */
+} iha_problem;
+
+/* Supported head widths d = D/H: IHA_BF16 takes 64 and 128; IHA_F32 takes
+ * 16, 32, 64 and 128.  H is at most 64. */
+
+/* Bytes of workspace iha_forward needs for this problem (written to *bytes).
+ * Validates the problem like iha_forward does. */
+iha_status iha_workspace_bytes(const iha_problem* prob, size_t* bytes);
+
+/* The IHA forward pass (Algorithm 1) on `stream`.
+ * X, W_Q, W_K, W_V: device, dtype prob->dtype.  alpha_*, R: device float.
+ * X_out: device float [B][N][D].  workspace: device, >= iha_workspace_bytes(),
+ * 256-byte aligned. */
+iha_status iha_forward(const iha_problem* prob, const void* X, const void* W_Q, const void* W_K,
+                       const void* W_V, const float* alpha_Q, const float* alpha_K,
+                       const float* alpha_V, const float* R, float* X_out, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/* iha_forward that also records events[0..4] on `stream` around its steps:
+ * [0] start, [1] after mixing (weight fold and input conversion), [2] after
+ * the projection GEMM, [3] after attention, [4] after the collapse.  The
+ * events are created by the caller (hipEventCreate) and must not be NULL. */
+iha_status iha_forward_timed(const iha_problem* prob, const void* X, const void* W_Q,
+                             const void* W_K, const void* W_V, const float* alpha_Q,
+                             const float* alpha_K, const float* alpha_V, const float* R,
+                             float* X_out, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream, hipEvent_t* events);
+
+/* The attention step alone (step 3 of Algorithm 1; textbook eq. 5.3 and 5.11),
+ * for already stacked, interleaved tensors of stacked length L:
+ *   Q, K   fp16 [B][L][H][d]   (row i = stacked position i)
+ *   Vt     fp16 [B][H][d][L]   (values, channel-major)
+ *   O      float [B][L][H][d]  O[i] = sum_{i' visible} softmax_i'(s) V[i']
+ * with scores s = (q_i . k_i') * score_scale.  The kernel works in base 2, so
+ * pass score_scale = log2(e)/sqrt(d) for the textbook's softmax(QK^T/sqrt(d)).
+ * mask/window as above on i.  d must be 64 or 128.  IHA_FLAG_CHECK in
+ * `flags` synchronises and reports an empty row (IHA_ERR_EMPTY_ROW); that
+ * needs a 256-byte device `flag_buf` (otherwise it may be NULL). */
+iha_status iha_attention(int64_t B, int64_t L, int64_t H, int64_t d, int32_t mask,
+                         int64_t window, float score_scale, const void* Q, const void* K,
+                         const void* Vt, float* O, uint32_t flags, void* flag_buf,
+                         hipStream_t stream);
+
+/* Static, human-readable name of a status code. */
+const char* iha_status_str(iha_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* IHA_H */

@@ -1,0 +1,161 @@
+// Step 1 of Algorithm 1 ("Interleaved Head Attention" page, section 4): pseudo-head
+// mixing.  Since Q~_{h,j} = sum_m alpha_{m,h,j} X W^(m) = X (sum_m alpha_{m,h,j} W^(m)),
+// the mixing is applied once to the weights (fp32 arithmetic) and the projection
+// becomes one plain GEMM against the folded weights.
+//
+// Folded weight layout: Wt[col][k], col in [0, 3*P*H*d), k in [0, D) contiguous
+// (both GEMM operands then carry the contraction index contiguously).
+//   Q, K blocks: col = (j*H + h)*d + c  -> the GEMM writes [tokens][P][H][d], i.e. the
+//                                          interleaved stacked rows t*P + j directly.
+//   V block:     col = (h*d + c)*P + j  -> for fixed (h, c) the P outputs of a token
+//                                          are adjacent, which the GEMM uses to write
+//                                          the channel-major V^T [B][H][d][P*N].
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace iha {
+namespace {
+
+constexpr int kFoldK = 32;   // rows of W (contraction index k) per block
+constexpr int kFoldC = 8;    // head channels c per block
+constexpr int kFoldThreads = kFoldK * kFoldC;
+
+template <typename Tin>
+__device__ __forceinline__ float load_w(const Tin* p);
+template <>
+__device__ __forceinline__ float load_w<uint16_t>(const uint16_t* p) { return bf16_to_float(*p); }
+template <>
+__device__ __forceinline__ float load_w<float>(const float* p) { return *p; }
+
+template <typename Tout>
+__device__ __forceinline__ Tout store_cvt(float v);
+template <>
+__device__ __forceinline__ half_t store_cvt<half_t>(float v) { return static_cast<half_t>(v); }
+template <>
+__device__ __forceinline__ float store_cvt<float>(float v) { return v; }
+
+// grid: (ceil(D / 32), d / 8, 3 = Q/K/V).  block: 256 threads.
+// Dynamic LDS: H * 8 * 32 floats holding W[k0..k0+32)[m*d + c0 .. +8) for every source head m,
+// stored as [m][c][k] so that the 32 lanes reading one c see consecutive k.
+template <typename Tin, typename Tout>
+__global__ __launch_bounds__(kFoldThreads) void fold_kernel(FoldArgs a) {
+  extern __shared__ float wsh[];
+  const int which = blockIdx.z;
+  const Tin* W = static_cast<const Tin*>(a.W[which]);
+  const float* alpha = a.alpha[which];
+  const int D = a.D, H = a.H, d = a.d, P = a.P;
+  const int HD = H * d;
+  const int k0 = blockIdx.x * kFoldK;
+  const int c0 = blockIdx.y * kFoldC;
+  const int tid = threadIdx.x;
+
+  if (which == 0 && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0 && a.flag) *a.flag = 0u;
+
+  // Load: element e -> (m, kk, cc) with cc fastest (8 consecutive channels of one W row).
+  for (int e = tid; e < H * kFoldK * kFoldC; e += kFoldThreads) {
+    const int m = e / (kFoldK * kFoldC);
+    const int kk = (e / kFoldC) % kFoldK;
+    const int cc = e % kFoldC;
+    const int k = k0 + kk;
+    float v = 0.f;
+    if (k < D) v = load_w<Tin>(W + static_cast<int64_t>(k) * HD + m * d + c0 + cc);
+    wsh[(m * kFoldC + cc) * kFoldK + kk] = v;
+  }
+  __syncthreads();
+
+  const int kk = tid % kFoldK;
+  const int cc = tid / kFoldK;
+  const int k = k0 + kk;
+  const int c = c0 + cc;
+  const int PHd = P * H * d;
+  Tout* Wt = static_cast<Tout*>(a.Wt) + static_cast<int64_t>(which) * PHd * D;
+  const float scale = a.out_scale[which];
+  if (k >= D) return;
+  for (int h = 0; h < H; ++h) {
+    for (int j = 0; j < P; ++j) {
+      float acc = 0.f;
+      for (int m = 0; m < H; ++m)
+        acc = fmaf(alpha[(m * H + h) * P + j], wsh[(m * kFoldC + cc) * kFoldK + kk], acc);
+      const int col = (which < 2) ? (j * H + h) * d + c : (h * d + c) * P + j;
+      Wt[static_cast<int64_t>(col) * D + k] = store_cvt<Tout>(acc * scale);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void cvt_bf16_f16_kernel(const uint4* __restrict__ x,
+                                                           uint4* __restrict__ y, int64_t n8) {
+  for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < n8; i += static_cast<int64_t>(gridDim.x) * 256) {
+    const uint4 v = x[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const half_t lo = static_cast<half_t>(__uint_as_float(w[q] << 16));
+      const half_t hi = static_cast<half_t>(__uint_as_float(w[q] & 0xFFFF0000u));
+      o[q] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+    }
+    y[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+__global__ void cvt_tail_kernel(const uint16_t* x, half_t* y, int64_t start, int64_t n) {
+  const int64_t i = start + blockIdx.x * 64LL + threadIdx.x;
+  if (i < n) y[i] = static_cast<half_t>(bf16_to_float(x[i]));
+}
+
+__global__ void clear_flag_kernel(unsigned* flag) { *flag = 0u; }
+
+__global__ __launch_bounds__(256) void check_finite_kernel(const float* __restrict__ x, int64_t n,
+                                                           unsigned* flag) {
+  bool bad = false;
+  for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256)
+    bad |= !__builtin_isfinite(x[i]);
+  if (bad) atomicOr(flag, kFlagNonFinite);
+}
+
+template <typename Tin, typename Tout>
+hipError_t launch_fold_impl(const FoldArgs& a, hipStream_t s) {
+  const dim3 grid((a.D + kFoldK - 1) / kFoldK, a.d / kFoldC, 3);
+  const size_t lds = static_cast<size_t>(a.H) * kFoldK * kFoldC * sizeof(float);
+  hipLaunchKernelGGL((fold_kernel<Tin, Tout>), grid, dim3(kFoldThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fold_bf16(const FoldArgs& a, hipStream_t s) {
+  return launch_fold_impl<uint16_t, half_t>(a, s);
+}
+hipError_t launch_fold_f32(const FoldArgs& a, hipStream_t s) {
+  return launch_fold_impl<float, float>(a, s);
+}
+
+hipError_t launch_cvt_bf16_f16(const uint16_t* x, void* y, int64_t n, hipStream_t s) {
+  const int64_t n8 = n / 8;
+  if (n8 > 0) {
+    const int64_t blocks = std::min<int64_t>((n8 + 255) / 256, 256 * 16);
+    hipLaunchKernelGGL(cvt_bf16_f16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                       reinterpret_cast<const uint4*>(x), static_cast<uint4*>(y), n8);
+  }
+  if (n8 * 8 < n) {
+    const int64_t rest = n - n8 * 8;
+    hipLaunchKernelGGL(cvt_tail_kernel, dim3(static_cast<unsigned>((rest + 63) / 64)), dim3(64), 0,
+                       s, x, static_cast<half_t*>(y), n8 * 8, n);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_clear_flag(unsigned* flag, hipStream_t s) {
+  hipLaunchKernelGGL(clear_flag_kernel, dim3(1), dim3(1), 0, s, flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_finite(const float* x, int64_t n, unsigned* flag, hipStream_t s) {
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 256 * 8));
+  hipLaunchKernelGGL(check_finite_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, x,
+                     n, flag);
+  return hipGetLastError();
+}
+
+}  // namespace iha

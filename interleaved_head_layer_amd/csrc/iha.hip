@@ -1,0 +1,269 @@
+// Host side of the C ABI declared in include/iha.h: argument validation, workspace
+// layout and the launch sequence of the IHA forward pass (Algorithm 1 of the
+// "Interleaved Head Attention" page, section 4).
+#include "iha.h"
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxH = 64;
+constexpr int64_t kMaxRows = int64_t(1) << 30;   // B*N tokens and P*N stacked rows
+constexpr int64_t kMaxElems = int64_t(1) << 40;  // elements of any one tensor
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t flag, xh, wt, q, k, vt, pbar, total;
+};
+
+bool d_supported(int32_t dtype, int64_t d) {
+  if (dtype == IHA_BF16) return d == 64 || d == 128;
+  return d == 16 || d == 32 || d == 64 || d == 128;
+}
+
+iha_status validate(const iha_problem* p) {
+  if (!p) return IHA_ERR_INVALID_ARG;
+  if (p->B < 1 || p->N < 1 || p->D < 1 || p->H < 1 || p->P < 1) return IHA_ERR_INVALID_ARG;
+  if (p->mask < IHA_MASK_NONE || p->mask > IHA_MASK_WINDOW) return IHA_ERR_INVALID_ARG;
+  if (p->dtype != IHA_F32 && p->dtype != IHA_BF16) return IHA_ERR_INVALID_ARG;
+  if ((p->flags & ~IHA_FLAG_CHECK) != 0 || p->reserved != 0) return IHA_ERR_INVALID_ARG;
+  if (p->D % p->H != 0) return IHA_ERR_SHAPE;
+  if (p->H > kMaxH || p->H * p->H * p->P > 16384) return IHA_ERR_UNSUPPORTED;
+  if (!d_supported(p->dtype, p->D / p->H)) return IHA_ERR_UNSUPPORTED;
+  if (p->B * p->N > kMaxRows || p->P * p->N > kMaxRows || p->P > kMaxRows) return IHA_ERR_SHAPE;
+  if (p->B * p->N * p->P * p->D > kMaxElems / 4 || 3 * p->P * p->D * p->D > kMaxElems / 4)
+    return IHA_ERR_SHAPE;
+  // Every row of a window mask of width < 1 is empty (textbook section 5.3: a legal query
+  // with an empty allowed set is an error).
+  if (p->mask == IHA_MASK_WINDOW && p->window < 1) return IHA_ERR_EMPTY_ROW;
+  return IHA_OK;
+}
+
+Layout layout_of(const iha_problem& p) {
+  const size_t e = p.dtype == IHA_BF16 ? 2 : 4;
+  const size_t d = static_cast<size_t>(p.D / p.H);
+  const size_t rows = static_cast<size_t>(p.B) * p.P * p.N;  // stacked rows over the batch
+  const size_t act = rows * p.H * d;                         // elements of Q~, K~, V~, P-bar
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.flag = take(kAlign);
+  L.xh = p.dtype == IHA_BF16 ? take(static_cast<size_t>(p.B) * p.N * p.D * 2) : 0;
+  L.wt = take(3 * static_cast<size_t>(p.P) * p.D * p.D * e);
+  L.q = take(act * e);
+  L.k = take(act * e);
+  L.vt = take(act * e);
+  L.pbar = take(act * 4);
+  L.total = off;
+  return L;
+}
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("IHA_LOG");
+    return v && v[0] == '1';
+  }();
+  return on;
+}
+
+#define IHA_HIP(call)                                                              \
+  do {                                                                             \
+    hipError_t e_ = (call);                                                        \
+    if (e_ != hipSuccess) {                                                        \
+      if (log_enabled()) std::fprintf(stderr, "[iha] %s: %s\n", #call, hipGetErrorString(e_)); \
+      return IHA_ERR_DEVICE;                                                       \
+    }                                                                              \
+  } while (0)
+
+iha_status read_flag(const unsigned* flag, hipStream_t stream) {
+  unsigned host = 0;
+  IHA_HIP(hipStreamSynchronize(stream));
+  IHA_HIP(hipMemcpy(&host, flag, sizeof(host), hipMemcpyDeviceToHost));
+  if (host & iha::kFlagEmptyRow) return IHA_ERR_EMPTY_ROW;
+  if (host & iha::kFlagNonFinite) return IHA_ERR_NONFINITE;
+  return IHA_OK;
+}
+
+iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q, const void* W_K,
+                        const void* W_V, const float* alpha_Q, const float* alpha_K,
+                        const float* alpha_V, const float* R, float* X_out, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream, hipEvent_t* ev) {
+  const iha_status v = validate(prob);
+  if (v != IHA_OK) return v;
+  if (!X || !W_Q || !W_K || !W_V || !alpha_Q || !alpha_K || !alpha_V || !R || !X_out)
+    return IHA_ERR_INVALID_ARG;
+  const iha_problem& p = *prob;
+  const Layout lay = layout_of(p);
+  if (!workspace || workspace_bytes < lay.total ||
+      reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return IHA_ERR_WORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  unsigned* flag = reinterpret_cast<unsigned*>(ws + lay.flag);
+  const int B = static_cast<int>(p.B), N = static_cast<int>(p.N), D = static_cast<int>(p.D);
+  const int H = static_cast<int>(p.H), P = static_cast<int>(p.P), d = D / H;
+  const bool bf16 = p.dtype == IHA_BF16;
+  if (log_enabled())
+    std::fprintf(stderr, "[iha] forward B=%d N=%d D=%d H=%d d=%d P=%d mask=%d window=%lld dtype=%s\n",
+                 B, N, D, H, d, P, p.mask, static_cast<long long>(p.window), bf16 ? "bf16" : "f32");
+
+  if (ev) IHA_HIP(hipEventRecord(ev[0], stream));
+  // Step 1: mixing folded into the weights; bf16 X converted for the fp16 matrix cores.
+  iha::FoldArgs fa{};
+  fa.W[0] = W_Q;
+  fa.W[1] = W_K;
+  fa.W[2] = W_V;
+  fa.alpha[0] = alpha_Q;
+  fa.alpha[1] = alpha_K;
+  fa.alpha[2] = alpha_V;
+  fa.out_scale[0] = fa.out_scale[1] = fa.out_scale[2] = 1.f;
+  fa.Wt = ws + lay.wt;
+  fa.flag = flag;
+  fa.D = D;
+  fa.H = H;
+  fa.d = d;
+  fa.P = P;
+  IHA_HIP(bf16 ? iha::launch_fold_bf16(fa, stream) : iha::launch_fold_f32(fa, stream));
+  if (bf16)
+    IHA_HIP(iha::launch_cvt_bf16_f16(static_cast<const uint16_t*>(X), ws + lay.xh,
+                                     static_cast<int64_t>(B) * N * D, stream));
+  if (ev) IHA_HIP(hipEventRecord(ev[1], stream));
+
+  // Step 2: projection GEMM into the stacked layouts.
+  iha::GemmArgs g{};
+  g.A = bf16 ? static_cast<const void*>(ws + lay.xh) : X;
+  g.Bt = ws + lay.wt;
+  g.Q = ws + lay.q;
+  g.K = ws + lay.k;
+  g.Vt = ws + lay.vt;
+  g.M = B * N;
+  g.Kdim = D;
+  g.Ncol = 3 * P * H * d;
+  g.PHd = P * H * d;
+  g.Ntok = N;
+  g.P = P;
+  g.H = H;
+  g.d = d;
+  IHA_HIP(bf16 ? iha::launch_gemm_f16(g, stream) : iha::launch_gemm_f32(g, stream));
+  if (ev) IHA_HIP(hipEventRecord(ev[2], stream));
+
+  // Step 3: per-head masked attention over the P*N stacked rows.
+  iha::AttnArgs at{};
+  at.Q = ws + lay.q;
+  at.K = ws + lay.k;
+  at.Vt = ws + lay.vt;
+  at.O = reinterpret_cast<float*>(ws + lay.pbar);
+  at.flag = flag;
+  at.B = B;
+  at.L = P * N;
+  at.H = H;
+  at.d = d;
+  at.mask = p.mask;
+  at.window = p.mask == IHA_MASK_WINDOW
+                  ? static_cast<int>(p.window < at.L ? p.window : static_cast<int64_t>(at.L))
+                  : 0;
+  at.qk_scale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
+  IHA_HIP(bf16 ? iha::launch_attn_f16(at, stream) : iha::launch_attn_f32(at, stream));
+  if (ev) IHA_HIP(hipEventRecord(ev[3], stream));
+
+  // Steps 4-5: unstack, collapse with R, concatenate heads.
+  IHA_HIP(iha::launch_collapse(at.O, R, X_out, B * N, H, P, d, stream));
+  if (ev) IHA_HIP(hipEventRecord(ev[4], stream));
+
+  if (p.flags & IHA_FLAG_CHECK) {
+    IHA_HIP(iha::launch_check_finite(X_out, static_cast<int64_t>(B) * N * D, flag, stream));
+    return read_flag(flag, stream);
+  }
+  return IHA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+iha_status iha_workspace_bytes(const iha_problem* prob, size_t* bytes) {
+  if (!bytes) return IHA_ERR_INVALID_ARG;
+  const iha_status v = validate(prob);
+  if (v != IHA_OK) return v;
+  *bytes = layout_of(*prob).total;
+  return IHA_OK;
+}
+
+iha_status iha_forward(const iha_problem* prob, const void* X, const void* W_Q, const void* W_K,
+                       const void* W_V, const float* alpha_Q, const float* alpha_K,
+                       const float* alpha_V, const float* R, float* X_out, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  return forward_impl(prob, X, W_Q, W_K, W_V, alpha_Q, alpha_K, alpha_V, R, X_out, workspace,
+                      workspace_bytes, stream, nullptr);
+}
+
+iha_status iha_forward_timed(const iha_problem* prob, const void* X, const void* W_Q,
+                             const void* W_K, const void* W_V, const float* alpha_Q,
+                             const float* alpha_K, const float* alpha_V, const float* R,
+                             float* X_out, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream, hipEvent_t* events) {
+  if (!events) return IHA_ERR_INVALID_ARG;
+  for (int i = 0; i < 5; ++i)
+    if (!events[i]) return IHA_ERR_INVALID_ARG;
+  return forward_impl(prob, X, W_Q, W_K, W_V, alpha_Q, alpha_K, alpha_V, R, X_out, workspace,
+                      workspace_bytes, stream, events);
+}
+
+iha_status iha_attention(int64_t B, int64_t L, int64_t H, int64_t d, int32_t mask, int64_t window,
+                         float score_scale, const void* Q, const void* K, const void* Vt, float* O,
+                         uint32_t flags, void* flag_buf, hipStream_t stream) {
+  if (B < 1 || L < 1 || H < 1 || mask < IHA_MASK_NONE || mask > IHA_MASK_WINDOW)
+    return IHA_ERR_INVALID_ARG;
+  if (!Q || !K || !Vt || !O || !(score_scale > 0.f) || !std::isfinite(score_scale))
+    return IHA_ERR_INVALID_ARG;
+  if ((flags & ~IHA_FLAG_CHECK) != 0) return IHA_ERR_INVALID_ARG;
+  if ((flags & IHA_FLAG_CHECK) && !flag_buf) return IHA_ERR_WORKSPACE;
+  if (d != 64 && d != 128) return IHA_ERR_UNSUPPORTED;
+  if (L > kMaxRows || B * L * H * d > kMaxElems / 4) return IHA_ERR_SHAPE;
+  if (mask == IHA_MASK_WINDOW && window < 1) return IHA_ERR_EMPTY_ROW;
+  unsigned* flag = static_cast<unsigned*>(flag_buf);
+  if (flag) IHA_HIP(iha::launch_clear_flag(flag, stream));
+  iha::AttnArgs at{};
+  at.Q = Q;
+  at.K = K;
+  at.Vt = Vt;
+  at.O = O;
+  at.flag = flag;
+  at.B = static_cast<int>(B);
+  at.L = static_cast<int>(L);
+  at.H = static_cast<int>(H);
+  at.d = static_cast<int>(d);
+  at.mask = mask;
+  at.window = mask == IHA_MASK_WINDOW ? static_cast<int>(window < L ? window : L) : 0;
+  at.qk_scale = score_scale;
+  IHA_HIP(iha::launch_attn_f16(at, stream));
+  if (flags & IHA_FLAG_CHECK) return read_flag(flag, stream);
+  return IHA_OK;
+}
+
+const char* iha_status_str(iha_status s) {
+  switch (s) {
+    case IHA_OK: return "IHA_OK";
+    case IHA_ERR_INVALID_ARG: return "IHA_ERR_INVALID_ARG: invalid argument";
+    case IHA_ERR_SHAPE: return "IHA_ERR_SHAPE: D not a multiple of H, or size out of range";
+    case IHA_ERR_EMPTY_ROW: return "IHA_ERR_EMPTY_ROW: a query has no visible key";
+    case IHA_ERR_NONFINITE: return "IHA_ERR_NONFINITE: non-finite value in the output";
+    case IHA_ERR_WORKSPACE: return "IHA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case IHA_ERR_UNSUPPORTED: return "IHA_ERR_UNSUPPORTED: head width or head count not supported";
+    case IHA_ERR_DEVICE: return "IHA_ERR_DEVICE: a HIP call failed";
+  }
+  return "IHA_ERR_UNKNOWN";
+}
+
+}  // extern "C"

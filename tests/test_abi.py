@@ -1,0 +1,91 @@
+"""The C-ABI library: it loads, exports every entry point include/iha.h declares, and its
+host-side validation returns the documented codes before touching the GPU.  No kernel is
+launched here (these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from interleaved_head_layer_amd import _binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "iha.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(iha_[a-z_]+)\s*\(", src)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    assert os.path.exists(bd.LIB_PATH), "run __graft_entry__.build() first"
+    lib = bd.load_library()
+    names = declared_functions()
+    assert {"iha_forward", "iha_workspace_bytes", "iha_status_str", "iha_attention",
+            "iha_forward_timed"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code, name in enumerate(bd.STATUS_NAMES):
+        assert bd.iha_status_str(code).startswith(name)
+
+
+def _ws(B=2, N=100, D=256, H=2, P=2, mask="window", window=None, dtype=bd.IHA_BF16, flags=0):
+    p = bd.make_problem(B, N, D, H, P, mask, window, dtype, flags)
+    n = ctypes.c_size_t(0)
+    return bd.load_library().iha_workspace_bytes(ctypes.byref(p), ctypes.byref(n)), n.value
+
+
+def test_workspace_size_covers_the_intermediates():
+    st, n = _ws()
+    assert st == bd.IHA_OK
+    B, N, D, P = 2, 100, 256, 2
+    rows = B * N * P
+    need = B * N * D * 2 + 3 * P * D * D * 2 + 3 * rows * D * 2 + rows * D * 4
+    assert need <= n <= need + 16 * 256
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=250, H=3), bd.STATUS_NAMES.index("IHA_ERR_SHAPE")),
+    (dict(N=3, P=2, mask="window"), bd.STATUS_NAMES.index("IHA_ERR_EMPTY_ROW")),   # N // (2P) = 0
+    (dict(window=0), bd.STATUS_NAMES.index("IHA_ERR_EMPTY_ROW")),
+    (dict(D=96, H=3), bd.STATUS_NAMES.index("IHA_ERR_UNSUPPORTED")),               # d = 32 in bf16
+    (dict(D=48, H=3, dtype=bd.IHA_F32), bd.IHA_OK),                                # d = 16 in fp32
+    (dict(D=24, H=3, dtype=bd.IHA_F32), bd.STATUS_NAMES.index("IHA_ERR_UNSUPPORTED")),  # d = 8
+    (dict(D=130 * 64, H=130), bd.STATUS_NAMES.index("IHA_ERR_UNSUPPORTED")),       # H > 64
+    (dict(B=0), bd.STATUS_NAMES.index("IHA_ERR_INVALID_ARG")),
+    (dict(mask=7), bd.STATUS_NAMES.index("IHA_ERR_INVALID_ARG")),
+    (dict(flags=4), bd.STATUS_NAMES.index("IHA_ERR_INVALID_ARG")),
+])
+def test_validation_codes(kw, code):
+    st, _ = _ws(**kw)
+    assert st == code, (kw, bd.iha_status_str(st))
+
+
+def test_forward_rejects_before_any_launch():
+    """Null pointers and a short workspace are refused on the host (fake, never-dereferenced
+    pointer values are enough to show it)."""
+    lib = bd.load_library()
+    p = bd.make_problem(1, 64, 128, 2, 2, "causal")
+    fake = ctypes.c_void_p(4096)
+    args = [fake] * 9
+    st = lib.iha_forward(ctypes.byref(p), None, *args[:7], fake, fake, ctypes.c_size_t(1 << 40), None)
+    assert st == bd.STATUS_NAMES.index("IHA_ERR_INVALID_ARG")
+    st = lib.iha_forward(ctypes.byref(p), *args[:8], fake, fake, ctypes.c_size_t(16), None)
+    assert st == bd.STATUS_NAMES.index("IHA_ERR_WORKSPACE")
+    st = lib.iha_forward(ctypes.byref(p), *args[:8], fake, ctypes.c_void_p(4096 + 8),
+                         ctypes.c_size_t(1 << 40), None)
+    assert st == bd.STATUS_NAMES.index("IHA_ERR_WORKSPACE")     # misaligned
+    st = lib.iha_attention(1, 64, 2, 96, 0, 0, 1.0, fake, fake, fake, fake, 0, None, None)
+    assert st == bd.STATUS_NAMES.index("IHA_ERR_UNSUPPORTED")
+    st = lib.iha_attention(1, 64, 2, 128, 2, 0, 1.0, fake, fake, fake, fake, 0, None, None)
+    assert st == bd.STATUS_NAMES.index("IHA_ERR_EMPTY_ROW")
+    st = lib.iha_attention(1, 64, 2, 128, 0, 0, -1.0, fake, fake, fake, fake, 0, None, None)
+    assert st == bd.STATUS_NAMES.index("IHA_ERR_INVALID_ARG")
+    evs = (ctypes.c_void_p * 5)()
+    st = lib.iha_forward_timed(ctypes.byref(p), *args[:8], fake, fake, ctypes.c_size_t(1 << 40),
+                               None, evs)
+    assert st == bd.STATUS_NAMES.index("IHA_ERR_INVALID_ARG")   # null events

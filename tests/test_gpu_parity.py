@@ -1,0 +1,187 @@
+"""Parity of the HIP library against the CPU oracle on the same seeded inputs (GPU only).
+
+Bar: max |gpu - oracle| <= tol * RMS(oracle output), tol = 1e-4 for the fp32 path and
+2e-2 for the bf16 path (fp16 intermediates, fp32 accumulation).  RMS is taken over the
+compared tokens; for sampled full-size runs over the uniformly drawn tokens only (the
+forced first/last tokens have the largest outputs and would loosen the bar).
+
+Small shapes are compared element by element over the whole output; they span several
+query/key tiles (128/64 rows) and GEMM tiles (128) and end in ragged tails.  Full-size
+workloads are launched exactly as the benchmark launches them and checked on sampled
+tokens, which the oracle computes exactly (only the keys those tokens can see).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from interleaved_head_layer_amd import workloads as wl
+import interleaved_head_layer_amd as iha
+
+pytestmark = pytest.mark.gpu
+F32_TOL = 1e-4
+BF16_TOL = 2e-2
+DEV = "cuda:0"
+
+
+def note(msg):
+    print(f"[case] {msg}", file=sys.stderr, flush=True)
+
+
+def to_dev(x, w):
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    t = lambda a, d=dt: torch.from_numpy(a).to(DEV).to(d).contiguous()
+    return (t(x["X"]), t(x["WQ"]), t(x["WK"]), t(x["WV"]), t(x["aQ"], torch.float32),
+            t(x["aK"], torch.float32), t(x["aV"], torch.float32), t(x["R"], torch.float32))
+
+
+def gpu_forward(w, x, flags=0, X_override=None):
+    args = list(to_dev(x, w))
+    if X_override is not None:
+        args[0] = X_override
+    out = iha.iha_forward(*args, w.H, w.P, w.mask, w.window, flags=flags)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def oracle_forward(w, x, tokens=None):
+    return oracle.forward(x["X"], x["WQ"], x["WK"], x["WV"], x["aQ"], x["aK"], x["aV"], x["R"],
+                          w.H, w.P, w.mask, w.window, tokens=tokens)
+
+
+def check(gpu, ref, tol, rms=None, what=""):
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite output"
+    rms = float(np.sqrt(np.mean(ref ** 2))) if rms is None else rms
+    err = float(np.max(np.abs(gpu - ref)))
+    note(f"{what}: max|err| = {err:.3e}, RMS = {rms:.3e}, ratio = {err / rms:.3e} (bar {tol:g})")
+    assert err <= tol * rms, f"{what}: max|err|/RMS = {err / rms:.3e} > {tol}"
+    return err / rms
+
+
+# ------------------------------------------------------------------ whole output vs oracle
+def test_tiny_fp32_workload_full():
+    w = wl.WORKLOADS["tiny_f32_none"]
+    note(w.describe())
+    x = wl.make_inputs(w)
+    check(gpu_forward(w, x), oracle_forward(w, x), F32_TOL, what=w.name)
+
+
+def test_mha_causal_workload_full():
+    w = wl.WORKLOADS["mha_causal_bf16"]
+    note(w.describe())
+    x = wl.make_inputs(w)
+    check(gpu_forward(w, x), oracle_forward(w, x), BF16_TOL, what=w.name)
+
+
+SMALL = [
+    # B, N, D, H, P, mask, window, dtype
+    (1, 300, 256, 2, 2, "window", None, "bf16"),     # L = 600: ragged query/key/GEMM tiles
+    (2, 77, 128, 2, 3, "causal", None, "bf16"),      # d = 64, odd P, L = 231 (not a multiple of 8)
+    (1, 200, 256, 2, 1, "none", None, "bf16"),       # P = 1, no mask
+    (1, 130, 384, 3, 4, "window", 1, "bf16"),        # every row sees only itself
+    (2, 64, 256, 2, 2, "window", 100000, "bf16"),    # window beyond the sequence = causal
+    (1, 1, 128, 1, 2, "causal", None, "bf16"),       # a single token
+    (1, 257, 512, 4, 2, "window", 200, "bf16"),
+    (1, 150, 256, 2, 5, "none", None, "bf16"),       # P = 5, mask none over 750 rows
+    (3, 40, 640, 5, 2, "causal", None, "bf16"),      # H = 5
+    (2, 50, 64, 2, 3, "causal", None, "f32"),        # fp32 path, d = 32
+    (1, 70, 256, 2, 2, "window", 9, "f32"),          # fp32 path, d = 128
+    (1, 33, 64, 4, 2, "none", None, "f32"),          # fp32 path, d = 16
+]
+
+
+@pytest.mark.parametrize("B,N,D,H,P,mask,window,dtype", SMALL)
+def test_small_shapes_full(B, N, D, H, P, mask, window, dtype):
+    w = wl.custom(B, N, D, H, P, mask, dtype=dtype, seed=B * 1000 + N + P, window=window)
+    note(w.describe())
+    x = wl.make_inputs(w)
+    check(gpu_forward(w, x), oracle_forward(w, x), F32_TOL if dtype == "f32" else BF16_TOL,
+          what=w.name)
+
+
+# ------------------------------------------------------- full-size workloads, sampled tokens
+@pytest.mark.parametrize("name", wl.HEADLINE)
+def test_full_size_workload_sampled(name):
+    w = wl.WORKLOADS[name]
+    note(w.describe())
+    x = wl.make_inputs(w)
+    gpu = gpu_forward(w, x).reshape(w.B * w.N, w.D)
+    uniform = np.sort(np.random.default_rng(w.seed).choice(w.B * w.N, 24, replace=False))
+    edges = wl.sample_tokens(w, 0)
+    tokens = np.unique(np.concatenate([uniform, edges]))
+    ref = oracle_forward(w, x, tokens=tokens)
+    rms = float(np.sqrt(np.mean(ref[np.isin(tokens, uniform)] ** 2)))
+    check(gpu[tokens], ref, BF16_TOL, rms=rms, what=f"{name} ({len(tokens)} tokens)")
+    assert np.all(np.isfinite(gpu))
+
+
+# --------------------------------------------------------------- attention step alone
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask,window", [("none", 0), ("causal", 0), ("window", 37)])
+def test_attention_step_vs_oracle(d, mask, window):
+    """iha_attention on generator-made fp16 stacked Q, K, V against the oracle's attention core
+    (textbook Algorithm 5.1) per (b, h), on every row."""
+    B, L, H = 2, 333, 2
+    q, k, v = wl.make_stacked_qkv(B, L, H, d, seed=d + len(mask), scale=1.0)
+    note(f"attention B={B} L={L} H={H} d={d} mask={mask} window={window}")
+    Q = torch.from_numpy(q).to(DEV).half()
+    K = torch.from_numpy(k).to(DEV).half()
+    Vt = torch.from_numpy(np.ascontiguousarray(v.transpose(0, 2, 3, 1))).to(DEV).half()
+    O = iha.iha_attention(Q, K, Vt, mask, window).cpu().numpy().astype(np.float64)
+    code = {"none": oracle.MASK_NONE, "causal": oracle.MASK_CAUSAL, "window": oracle.MASK_WINDOW}[mask]
+    ref = np.zeros_like(O)
+    for b in range(B):
+        for h in range(H):
+            ref[b, :, h], _, _ = oracle.attention(q[b, :, h], k[b, :, h], v[b, :, h], code, window)
+    check(O, ref, BF16_TOL, what=f"attention d={d} {mask}")
+
+
+# --------------------------------------------------------------------- properties on GPU
+def test_bitwise_deterministic():
+    w = wl.custom(2, 300, 512, 4, 2, "window", seed=77)
+    note(w.describe())
+    x = wl.make_inputs(w)
+    a, b = gpu_forward(w, x), gpu_forward(w, x)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("mask", ["causal", "window"])
+def test_future_perturbation_leaves_past_bitwise(mask):
+    """Textbook section 5.4: changing inputs after token t0 leaves outputs up to t0 unchanged."""
+    w = wl.custom(1, 400, 256, 2, 2, mask, seed=5, window=64 if mask == "window" else None)
+    note(w.describe())
+    x = wl.make_inputs(w)
+    a = gpu_forward(w, x)
+    x2 = dict(x)
+    X2 = x["X"].copy()
+    t0 = 150
+    X2[:, t0 + 1:] = wl.round_to_bf16(X2[:, t0 + 1:] * 1.5 + 0.25)
+    x2["X"] = X2
+    b = gpu_forward(w, x2)
+    assert np.array_equal(a[:, :t0 + 1], b[:, :t0 + 1])
+    assert not np.allclose(a[:, t0 + 1:], b[:, t0 + 1:])
+
+
+def test_nonfinite_input_reported_with_check_flag():
+    w = wl.custom(1, 64, 256, 2, 2, "causal", seed=3)
+    x = wl.make_inputs(w)
+    x["X"] = x["X"].copy()
+    x["X"][0, 10, 3] = np.nan
+    note("NaN input, IHA_FLAG_CHECK")
+    with pytest.raises(iha.IHAError) as e:
+        gpu_forward(w, x, flags=iha.IHA_FLAG_CHECK)
+    assert "NONFINITE" in str(e.value)
+    ok = wl.make_inputs(w)
+    gpu_forward(w, ok, flags=iha.IHA_FLAG_CHECK)     # clean input passes the check
+
+
+def test_empty_window_is_rejected():
+    w = wl.custom(1, 3, 128, 1, 2, "window", seed=3)   # N // (2P) = 0
+    assert w.window == 0
+    x = wl.make_inputs(w)
+    with pytest.raises(iha.IHAError) as e:
+        gpu_forward(w, x)
+    assert "EMPTY_ROW" in str(e.value)
