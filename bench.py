@@ -81,7 +81,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     for e in evs:               # create the events before the timed region
         for ev in e:
             ev.record()
@@ -94,7 +94,7 @@ def main():
     assert bool(torch.isfinite(out).all()), "non-finite output"
 
     ms_step = (t1 - t0) * 1e3 / args.steps
-    names = ["fold", "gemm", "attention", "collapse"]
+    names = ["fold", "gemm", "attention", "first_rows", "collapse"]
     kms = {n: float(np.mean([evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)]))
            for k, n in enumerate(names)}
 
@@ -120,6 +120,7 @@ def main():
              "gemm": roof("mfma", proj_flops, kms["gemm"]),
              "attention": roof("mfma", attn_flops, kms["attention"]),
              "collapse": roof("hbm", collapse_bytes, kms["collapse"])}
+    first_rows_ms = kms["first_rows"]
     dominant = max(kms, key=kms.get)
     value = B * P * N / (ms_step * 1e-3)
 

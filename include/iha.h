@@ -39,7 +39,10 @@
  * into the weights in fp32, the folded weights, the projected Q/K/V and the
  * attention probabilities are stored as fp16 for the matrix cores (fp32
  * accumulation), softmax state and the per-head attention output are fp32,
- * and X_out is fp32.
+ * and X_out is fp32.  Under a causal or window mask the first 128 stacked
+ * rows of every (b, h) see the fewest keys and have the largest outputs; they
+ * are recomputed with fp32 intermediates (exact bf16 projection, fp32 mixing
+ * and attention) so that their absolute error matches the other rows'.
  *
  * Ownership and streams.  The caller owns every buffer; all device pointers
  * must be on the current HIP device.  The library keeps no state between
@@ -113,10 +116,12 @@ iha_status iha_forward(const iha_problem* prob, const void* X, const void* W_Q, 
                        const float* alpha_V, const float* R, float* X_out, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 
-/* iha_forward that also records events[0..4] on `stream` around its steps:
+/* iha_forward that also records events[0..5] on `stream` around its steps:
  * [0] start, [1] after mixing (weight fold and input conversion), [2] after
- * the projection GEMM, [3] after attention, [4] after the collapse.  The
- * events are created by the caller (hipEventCreate) and must not be NULL. */
+ * the projection GEMM, [3] after the attention kernel, [4] after the fp32
+ * recomputation of the first stacked rows (no work for IHA_F32 or
+ * IHA_MASK_NONE), [5] after the collapse.  The events are created by the
+ * caller (hipEventCreate) and must not be NULL. */
 iha_status iha_forward_timed(const iha_problem* prob, const void* X, const void* W_Q,
                              const void* W_K, const void* W_V, const float* alpha_Q,
                              const float* alpha_K, const float* alpha_V, const float* R,

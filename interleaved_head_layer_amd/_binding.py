@@ -109,8 +109,9 @@ def iha_forward(X, W_Q, W_K, W_V, alpha_Q, alpha_K, alpha_V, R, H: int, P: int, 
     """IHA forward (Algorithm 1).  X [B, N, D] bf16 or fp32 on the GPU; W_* [D, D] same dtype;
     alpha_* [H, H, P] and R [H, H*P] fp32.  Returns X~ [B, N, D] fp32.
 
-    ``events``: optional list of 5 torch.cuda.Event(enable_timing=True), recorded around the
-    steps (start, mixing, GEMM, attention, collapse) on the current stream."""
+    ``events``: optional list of 6 torch.cuda.Event(enable_timing=True), recorded around the
+    steps (start, mixing, GEMM, attention, first-rows recomputation, collapse) on the current
+    stream."""
     import torch
     if X.dim() != 3:
         raise ValueError("X must be [B, N, D]")
@@ -137,12 +138,12 @@ def iha_forward(X, W_Q, W_K, W_V, alpha_Q, alpha_K, alpha_V, R, H: int, P: int, 
     if events is None:
         st = lib.iha_forward(ctypes.byref(prob), *args, stream)
     else:
-        if len(events) != 5:
-            raise ValueError("events must hold 5 torch.cuda.Event objects")
+        if len(events) != 6:
+            raise ValueError("events must hold 6 torch.cuda.Event objects")
         for e in events:
             if e.cuda_event == 0:     # create the underlying event
                 e.record()
-        evs = (ctypes.c_void_p * 5)(*[e.cuda_event for e in events])
+        evs = (ctypes.c_void_p * 6)(*[e.cuda_event for e in events])
         st = lib.iha_forward_timed(ctypes.byref(prob), *args, stream, evs)
     if st != IHA_OK:
         raise IHAError(st, "iha_forward")

@@ -42,63 +42,168 @@ __device__ __forceinline__ bool visible(int q, int k, int L, int window) {
   return true;
 }
 
+// K/V^T tile stages in LDS.  Rows are unpadded; 16-byte chunks are XOR-swizzled by row so
+// that the matrix-core operand reads of 16 lanes (16 different rows, same logical chunk)
+// hit 16 different bank groups.
 template <int DH>
 struct AttnSmem {
-  static constexpr int KLD = DH + 8;   // K tile row stride (halves)
-  static constexpr int VLD = ABN + 8;  // V^T tile row stride (halves)
-  half_t k[ABN * KLD];
-  half_t v[DH * VLD];
+  static constexpr int KLD = DH;   // K tile row (halves)
+  static constexpr int VLD = ABN;  // V^T tile row (halves)
+  half_t k[2][ABN * KLD];
+  half_t v[2][DH * VLD];
 };
 
+// K rows: chunk c of row r sits at position c ^ kswz(r).  The score product reads rows
+// sigma(l) of 16 lanes = {0-3, 16-19, 4-7, 20-23} (+8): bits 0-2 and bit 4 of r spread them.
 template <int DH>
-__device__ __forceinline__ void attn_load_tile(const half_t* __restrict__ Kb,
-                                               const half_t* __restrict__ Vb, int64_t rs, int L,
-                                               int k0, uint4 (&kr)[DH / 32], uint4 (&vr)[DH / 32]) {
-  const int tid = threadIdx.x;
-  constexpr int KCH = DH / 8;  // 16-byte chunks per K row
+__device__ __forceinline__ int kswz(int r) {
+  return DH == 128 ? ((r & 7) | (((r >> 4) & 1) << 3)) : (r & 7);
+}
+// V^T rows (64 keys = 128 bytes, two rows per 256-byte bank line): chunk c at c ^ ((r >> 1) & 7).
+__device__ __forceinline__ int vswz(int r) { return (r >> 1) & 7; }
+
+// Copy key tile [k0, k0 + 64) into one stage.  DIRECT: global -> LDS loads (no registers;
+// needs L % 8 == 0); otherwise through registers.  Keys past the end load a clamped valid row
+// and are masked out by the caller, so every value in LDS is finite.
+template <int DH, bool DIRECT>
+struct TileCopy {
+  static constexpr int KCH = DH / 8;                  // 16-byte chunks per K row
+  static constexpr int ROUNDS = DH / 32;              // (64 * DH * 2 bytes) / (256 lanes * 16 bytes)
+  uint4 kr[DIRECT ? 1 : ROUNDS], vr[DIRECT ? 1 : ROUNDS];
+
+  __device__ __forceinline__ void issue(const half_t* __restrict__ Kb, const half_t* __restrict__ Vb,
+                                        int64_t rs, int L, int k0, half_t* kst, half_t* vst) {
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
 #pragma unroll
-  for (int p = 0; p < DH / 32; ++p) {
-    const int idx = tid + AThreads * p;
-    const int row = idx / KCH, ch = idx % KCH;
-    const int key = k0 + row;
-    kr[p] = key < L ? *reinterpret_cast<const uint4*>(Kb + key * rs + ch * 8) : make_uint4(0, 0, 0, 0);
-  }
+    for (int p = 0; p < ROUNDS; ++p) {
+      // K: 16-byte slot (p*4 + w)*64 + lane of the stage -> row r, position pos.
+      const int slot = (p * 4 + w) * 64 + lane;
+      const int r = slot / KCH, pos = slot % KCH;
+      const int key = min(k0 + r, L - 1);
+      const half_t* ksrc = Kb + key * rs + (pos ^ kswz<DH>(r)) * 8;
+      // V^T: slot -> channel row cr (8 slots of 8 keys per row), position vpos.
+      const int cr = slot / (ABN / 8), vpos = slot % (ABN / 8);
+      int vkey = k0 + (vpos ^ vswz(cr)) * 8;
+      if (DIRECT) {
+        vkey = min(vkey, L - 8);
+        const half_t* vsrc = Vb + static_cast<int64_t>(cr) * L + vkey;
+        __builtin_amdgcn_global_load_lds(ksrc, (__attribute__((address_space(3))) void*)(kst + (p * 4 + w) * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vsrc, (__attribute__((address_space(3))) void*)(vst + (p * 4 + w) * 512), 16, 0, 0);
+      } else {
+        kr[p] = *reinterpret_cast<const uint4*>(ksrc);
+        const half_t* vsrc = Vb + static_cast<int64_t>(cr) * L + vkey;
+        uint16_t e[8];
 #pragma unroll
-  for (int p = 0; p < DH / 32; ++p) {
-    const int idx = tid + AThreads * p;
-    const int crow = idx / (ABN / 8), ch = idx % (ABN / 8);
-    const int key = k0 + ch * 8;
-    const half_t* src = Vb + static_cast<int64_t>(crow) * L + key;
-    if (key + 8 <= L && (L & 7) == 0) {
-      vr[p] = *reinterpret_cast<const uint4*>(src);
-    } else {
-      uint16_t e[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        e[q] = (key + q < L) ? __builtin_bit_cast(uint16_t, src[q]) : static_cast<uint16_t>(0);
-      vr[p] = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
-                         e[6] | (e[7] << 16));
+        for (int q = 0; q < 8; ++q)
+          e[q] = (vkey + q < L) ? __builtin_bit_cast(uint16_t, vsrc[q]) : static_cast<uint16_t>(0);
+        vr[p] = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
+                           e[6] | (e[7] << 16));
+      }
     }
   }
-}
-
-template <int DH>
-__device__ __forceinline__ void attn_store_tile(AttnSmem<DH>& sm, const uint4 (&kr)[DH / 32],
-                                                const uint4 (&vr)[DH / 32]) {
-  const int tid = threadIdx.x;
-  constexpr int KCH = DH / 8;
+  // Registers -> LDS (register path only).
+  __device__ __forceinline__ void commit(half_t* kst, half_t* vst) {
+    if (DIRECT) return;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
 #pragma unroll
-  for (int p = 0; p < DH / 32; ++p) {
-    const int idx = tid + AThreads * p;
-    *reinterpret_cast<uint4*>(&sm.k[(idx / KCH) * AttnSmem<DH>::KLD + (idx % KCH) * 8]) = kr[p];
-    *reinterpret_cast<uint4*>(&sm.v[(idx / (ABN / 8)) * AttnSmem<DH>::VLD + (idx % (ABN / 8)) * 8]) = vr[p];
+    for (int p = 0; p < ROUNDS; ++p) {
+      const int slot = (p * 4 + w) * 64 + lane;
+      *reinterpret_cast<uint4*>(kst + slot * 8) = kr[p];
+      *reinterpret_cast<uint4*>(vst + slot * 8) = vr[p];
+    }
   }
+};
+
+__device__ __forceinline__ void wait_global_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Running softmax state of one lane (one query row, shared with lane l^32).
+template <int NCB>
+struct RowState {
+  float m;          // stale running maximum of the raw scores q.k (-inf before any visible key)
+  float l;          // this lane's share of the running sum
+  floatx16 o[NCB];  // O^T accumulators
+};
+
+// Softmax rescaling threshold, base 2: the running maximum is only moved (and O, l rescaled)
+// when a new score exceeds it by more than this, so the probabilities fed to the matrix
+// cores stay <= 2^8 (fp16-safe) and the rescale is rare.  Shift invariance of softmax
+// makes any such choice of the subtracted maximum exact.
+constexpr float kRescaleLog2 = 8.f;
+
+// One key tile for one wave: S^T = K Q^T, (masked) online softmax, O^T += V^T P^T.
+template <int DH, int MASK, bool EDGE>
+__device__ __forceinline__ void attn_tile(const half_t* __restrict__ ks, const half_t* __restrict__ vs,
+                                          const half8 (&qf)[DH / 16], RowState<DH / 32>& st,
+                                          int k0, int qrow, int L, int window, float scale,
+                                          float thr, int krow, int l32, int hf) {
+  constexpr int KLD = AttnSmem<DH>::KLD, VLD = AttnSmem<DH>::VLD;
+  constexpr int NKS = DH / 16, NCB = DH / 32;
+  floatx16 s[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+    for (int kstep = 0; kstep < NKS; ++kstep) {
+      const int kr_ = kb * 32 + krow;
+      const half8 kf = *reinterpret_cast<const half8*>(&ks[kr_ * KLD + ((kstep * 2 + hf) ^ kswz<DH>(kr_)) * 8]);
+      s[kb] = mfma32(kf, qf[kstep], s[kb]);
+    }
+  }
+  if (EDGE) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (!visible<MASK>(qrow, k0 + kb * 32 + 16 * hf + r, L, window)) s[kb][r] = -__builtin_inff();
+  }
+  float mx = s[0][0];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  // A row moves its maximum only when a score exceeds it by more than 2^8 (or at its first
+  // visible key).  The decision is per row (alpha = 1 exactly for the others), so a row's
+  // result never depends on the other rows of the wave.
+  const bool need = mx > st.m + thr;
+  if (__any(need)) {
+    const float m_new = need ? mx : st.m;
+    const float alpha = !need ? 1.f : (st.m == -__builtin_inff()) ? 0.f : fast_exp2((st.m - m_new) * scale);
+    st.l *= alpha;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[cb][r] *= alpha;
+    st.m = m_new;
+  }
+  const float m_off = (st.m == -__builtin_inff()) ? 0.f : st.m * scale;
+  float psum = 0.f;
+  half8 pf[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = fast_exp2(fmaf(s[kb][r], scale, -m_off));
+      psum += p;
+      pf[kb][r >> 3][r & 7] = static_cast<half_t>(p);
+    }
+  st.l += psum;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int vr_ = cb * 32 + l32;
+        const half8 vf = *reinterpret_cast<const half8*>(&vs[vr_ * VLD + ((kb * 4 + 2 * hf + s2) ^ vswz(vr_)) * 8]);
+        st.o[cb] = mfma32(vf, pf[kb][s2], st.o[cb]);
+      }
 }
 
-template <int DH, int MASK>
+template <int DH, int MASK, bool DIRECT>
 __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) AttnSmem<DH> sm;
-  constexpr int KLD = AttnSmem<DH>::KLD, VLD = AttnSmem<DH>::VLD;
   constexpr int NKS = DH / 16;  // k-steps of the score product
   constexpr int NCB = DH / 32;  // 32-channel blocks of the output
   const int L = a.L, H = a.H, window = a.window;
@@ -139,105 +244,53 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
   const int kt0 = klo / ABN, kt1 = (khi + ABN - 1) / ABN;
 
   const float scale = a.qk_scale;
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;
-  floatx16 o[NCB];
+  const float thr = kRescaleLog2 / scale;
+  RowState<NCB> st;
+  st.m = -__builtin_inff();
+  st.l = 0.f;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[cb][r] = 0.f;
+    for (int r = 0; r < 16; ++r) st.o[cb][r] = 0.f;
 
-  uint4 kr[DH / 32], vr[DH / 32];
+  TileCopy<DH, DIRECT> cp;
   if (kt0 < kt1) {
-    attn_load_tile<DH>(Kb, Vb, rs, L, kt0 * ABN, kr, vr);
-    attn_store_tile<DH>(sm, kr, vr);
+    cp.issue(Kb, Vb, rs, L, kt0 * ABN, sm.k[0], sm.v[0]);
+    cp.commit(sm.k[0], sm.v[0]);
   }
+  wait_global_loads();
   __syncthreads();
 
   const int krow = sigma_row(l32);
   for (int kt = kt0; kt < kt1; ++kt) {
     const int k0 = kt * ABN;
-    if (kt + 1 < kt1) attn_load_tile<DH>(Kb, Vb, rs, L, k0 + ABN, kr, vr);
-
-    floatx16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const half8 kf = *reinterpret_cast<const half8*>(&sm.k[(kb * 32 + krow) * KLD + ks * 16 + 8 * hf]);
-        s[kb] = mfma32(kf, qf[ks], s[kb]);
-      }
-    }
-
-    // Visibility: only tiles that cross a mask edge or the end of the sequence test keys.
+    const int stage = (kt - kt0) & 1;
+    const bool more = kt + 1 < kt1;
+    // The other stage was last read before the previous barrier: refill it now.
+    if (more) cp.issue(Kb, Vb, rs, L, k0 + ABN, sm.k[stage ^ 1], sm.v[stage ^ 1]);
+    // Only tiles that cross a mask edge or the end of the sequence test keys.
     bool edge = (k0 + ABN > L);
     if (MASK != kMaskNone) edge |= (k0 + ABN - 1 > q0);
     if (MASK == kMaskWindow) edge |= (k0 <= q0 + ABM - 1 - window);
-    if (edge) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + 16 * hf + r;
-          if (!visible<MASK>(qrow, key, L, window)) s[kb][r] = -__builtin_inff();
-        }
-    }
-
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    // A row with nothing visible yet keeps m = -inf; its terms use offset 0 so that
-    // exp2(-inf - (-inf)) never happens.
-    const float m_off = (m_new == -__builtin_inff()) ? 0.f : m_new * scale;
-    const float alpha = fast_exp2(m_run * scale - m_off);
-    float psum = 0.f;
-    half8 pf[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(s[kb][r], scale, -m_off));
-        psum += p;
-        pf[kb][r >> 3][r & 7] = static_cast<half_t>(p);
-      }
-    l_run = fmaf(l_run, alpha, psum);
-    m_run = m_new;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[cb][r] *= alpha;
-
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const half8 vf = *reinterpret_cast<const half8*>(
-              &sm.v[(cb * 32 + l32) * VLD + kb * 32 + 16 * hf + 8 * s2]);
-          o[cb] = mfma32(vf, pf[kb][s2], o[cb]);
-        }
-
+    if (edge)
+      attn_tile<DH, MASK, true>(sm.k[stage], sm.v[stage], qf, st, k0, qrow, L, window, scale, thr, krow, l32, hf);
+    else
+      attn_tile<DH, MASK, false>(sm.k[stage], sm.v[stage], qf, st, k0, qrow, L, window, scale, thr, krow, l32, hf);
+    if (more) cp.commit(sm.k[stage ^ 1], sm.v[stage ^ 1]);
+    wait_global_loads();
     __syncthreads();
-    if (kt + 1 < kt1) {
-      attn_store_tile<DH>(sm, kr, vr);
-      __syncthreads();
-    }
   }
 
-  const float lt = l_run + __shfl_xor(l_run, 32);
+  const float lt = st.l + __shfl_xor(st.l, 32);
   if (qrow < L) {
-    float inv = 0.f;
+    // lt > 0 for every valid row; lt == 0 means nothing was visible (reported, output 0);
+    // a NaN sum (non-finite input) is passed through to the output.
+    float inv = lt;
     if (lt > 0.f) {
       inv = 1.f / lt;
-    } else if (a.flag) {
-      atomicOr(a.flag, kFlagEmptyRow);
+    } else if (lt == 0.f) {
+      inv = 0.f;
+      if (a.flag) atomicOr(a.flag, kFlagEmptyRow);
     }
     float* orow = Ob + qrow * rs;
 #pragma unroll
@@ -246,7 +299,7 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
       for (int q = 0; q < 4; ++q) {
         floatx4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = o[cb][4 * q + e] * inv;
+        for (int e = 0; e < 4; ++e) v[e] = st.o[cb][4 * q + e] * inv;
         *reinterpret_cast<floatx4*>(orow + cb * 32 + 8 * q + 4 * hf) = v;
       }
   }
@@ -293,13 +346,15 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnArgs a) {
     m = m_new;
   }
   if (i >= L) return;
-  float inv = 0.f;
+  float inv = l;  // NaN passes through
   if (l > 0.f) {
     inv = 1.f / l;
-  } else if (a.flag) {
-    atomicOr(a.flag, kFlagEmptyRow);
+  } else if (l == 0.f) {
+    inv = 0.f;
+    if (a.flag) atomicOr(a.flag, kFlagEmptyRow);
   }
-  float* orow = a.O + static_cast<int64_t>(b) * L * rs + h * DH + i * rs;
+  const int64_t obs = a.o_bstride ? a.o_bstride : static_cast<int64_t>(L) * rs;
+  float* orow = a.O + static_cast<int64_t>(b) * obs + h * DH + i * rs;
 #pragma unroll
   for (int c = 0; c < DH; ++c) orow[c] = o[c] * inv;
 }
@@ -307,7 +362,11 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnArgs a) {
 template <int DH, int MASK>
 hipError_t launch_f16_impl(const AttnArgs& a, hipStream_t s) {
   const int nqt = (a.L + ABM - 1) / ABM;
-  hipLaunchKernelGGL((attn_fwd_f16_kernel<DH, MASK>), dim3(nqt * a.H * a.B), dim3(AThreads), 0, s, a);
+  const dim3 grid(nqt * a.H * a.B);
+  if (a.L % 8 == 0)
+    hipLaunchKernelGGL((attn_fwd_f16_kernel<DH, MASK, true>), grid, dim3(AThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_f16_kernel<DH, MASK, false>), grid, dim3(AThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -3,6 +3,7 @@
 // "Interleaved Head Attention" page, section 4).
 #include "iha.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -20,7 +21,8 @@ constexpr int64_t kMaxElems = int64_t(1) << 40;  // elements of any one tensor
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t flag, xh, wt, q, k, vt, pbar, total;
+  size_t flag, xh, wt, q, k, vt, pbar, ye, qe, ke, vte, total;
+  int T0, R;  // precise first rows: tokens and stacked rows (0 when unused)
 };
 
 bool d_supported(int32_t dtype, int64_t d) {
@@ -65,6 +67,17 @@ Layout layout_of(const iha_problem& p) {
   L.k = take(act * e);
   L.vt = take(act * e);
   L.pbar = take(act * 4);
+  // bf16 inputs under a causal or window mask: fp32 recomputation of the first rows.
+  if (p.dtype == IHA_BF16 && p.mask != IHA_MASK_NONE) {
+    const int64_t R = std::min<int64_t>(iha::kPreciseRows, p.P * p.N);
+    const int64_t T0 = std::min<int64_t>(p.N, (R + p.P - 1) / p.P);
+    L.R = static_cast<int>(R);
+    L.T0 = static_cast<int>(T0);
+    L.ye = take(static_cast<size_t>(p.B) * T0 * 3 * p.D * 4);
+    L.qe = take(static_cast<size_t>(p.B) * R * p.D * 4);
+    L.ke = take(static_cast<size_t>(p.B) * R * p.D * 4);
+    L.vte = take(static_cast<size_t>(p.B) * R * p.D * 4);
+  }
   L.total = off;
   return L;
 }
@@ -176,10 +189,37 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
   at.qk_scale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
   IHA_HIP(bf16 ? iha::launch_attn_f16(at, stream) : iha::launch_attn_f32(at, stream));
   if (ev) IHA_HIP(hipEventRecord(ev[3], stream));
+  if (lay.R > 0) {
+    // The first stacked rows again, with fp32 intermediates (their outputs are the largest).
+    iha::EarlyArgs ea{};
+    ea.X = static_cast<const uint16_t*>(X);
+    ea.W[0] = static_cast<const uint16_t*>(W_Q);
+    ea.W[1] = static_cast<const uint16_t*>(W_K);
+    ea.W[2] = static_cast<const uint16_t*>(W_V);
+    ea.alpha[0] = alpha_Q;
+    ea.alpha[1] = alpha_K;
+    ea.alpha[2] = alpha_V;
+    ea.Y = reinterpret_cast<float*>(ws + lay.ye);
+    ea.Qe = reinterpret_cast<float*>(ws + lay.qe);
+    ea.Ke = reinterpret_cast<float*>(ws + lay.ke);
+    ea.Vte = reinterpret_cast<float*>(ws + lay.vte);
+    ea.B = B;
+    ea.N = N;
+    ea.D = D;
+    ea.H = H;
+    ea.d = d;
+    ea.P = P;
+    ea.T0 = lay.T0;
+    ea.R = lay.R;
+    IHA_HIP(iha::launch_early_qkv(ea, stream));
+    IHA_HIP(iha::launch_early_attn(ea, at.O, static_cast<int64_t>(at.L) * H * d, p.mask,
+                                   std::min(at.window, lay.R), at.qk_scale, stream));
+  }
+  if (ev) IHA_HIP(hipEventRecord(ev[4], stream));
 
   // Steps 4-5: unstack, collapse with R, concatenate heads.
   IHA_HIP(iha::launch_collapse(at.O, R, X_out, B * N, H, P, d, stream));
-  if (ev) IHA_HIP(hipEventRecord(ev[4], stream));
+  if (ev) IHA_HIP(hipEventRecord(ev[5], stream));
 
   if (p.flags & IHA_FLAG_CHECK) {
     IHA_HIP(iha::launch_check_finite(X_out, static_cast<int64_t>(B) * N * D, flag, stream));
@@ -214,7 +254,7 @@ iha_status iha_forward_timed(const iha_problem* prob, const void* X, const void*
                              float* X_out, void* workspace, size_t workspace_bytes,
                              hipStream_t stream, hipEvent_t* events) {
   if (!events) return IHA_ERR_INVALID_ARG;
-  for (int i = 0; i < 5; ++i)
+  for (int i = 0; i < 6; ++i)
     if (!events[i]) return IHA_ERR_INVALID_ARG;
   return forward_impl(prob, X, W_Q, W_K, W_V, alpha_Q, alpha_K, alpha_V, R, X_out, workspace,
                       workspace_bytes, stream, events);

@@ -37,8 +37,8 @@ struct GemmArgs {
 hipError_t launch_gemm_f16(const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s);
 
-// Masked attention over the stacked sequence: O = softmax_2(s) V with
-// s = (q . k) already in base-2 units (the score scale is folded into Q).
+// Masked attention over the stacked sequence: O = softmax_2(s) V with base-2 scores
+// s = (q . k) * qk_scale.
 struct AttnArgs {
   const void* Q;   // [B][L][H][d]
   const void* K;   // [B][L][H][d]
@@ -46,10 +46,31 @@ struct AttnArgs {
   float* O;        // [B][L][H][d]
   unsigned* flag;  // may be null
   int B, L, H, d, mask, window;
-  float qk_scale;  // multiplies q . k (1 when folded into Q)
+  float qk_scale;     // multiplies q . k to give base-2 scores
+  int64_t o_bstride;  // elements between batches of O (0: L*H*d)
 };
 hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
+
+// Full-precision recomputation of the first R stacked rows (R = min(128, P*N)) of every
+// (b, h) for bf16 inputs: exact bf16 projection of the first T0 = ceil(R/P) tokens
+// (fp32 accumulation), fp32 mixing into Qe, Ke [B][R][H][d] and Vte [B][H][d][R].
+struct EarlyArgs {
+  const uint16_t* X;      // [B][N][D] bf16
+  const uint16_t* W[3];   // [D][D] bf16
+  const float* alpha[3];  // [H][H][P]
+  float* Y;               // [B*T0][3*D]
+  float* Qe;
+  float* Ke;
+  float* Vte;
+  int B, N, D, H, d, P, T0, R;
+};
+hipError_t launch_early_qkv(const EarlyArgs& e, hipStream_t s);
+// fp32 attention of those rows (causal / window), written into O rows < R
+// (O [B][L][H][d] with batch stride o_bstride).
+hipError_t launch_early_attn(const EarlyArgs& e, float* O, int64_t o_bstride, int mask, int window,
+                             float scale, hipStream_t s);
+constexpr int kPreciseRows = 128;
 
 // Unstack + collapse + concatenation:
 //   out[tok][h*d + c] = sum_{h', j} R[h][h'*P + j] * Pbar[tok*P + j][h'][c]

@@ -45,7 +45,11 @@ def test_workspace_size_covers_the_intermediates():
     B, N, D, P = 2, 100, 256, 2
     rows = B * N * P
     need = B * N * D * 2 + 3 * P * D * D * 2 + 3 * rows * D * 2 + rows * D * 4
+    R, T0 = min(128, P * N), min(N, -(-128 // P))     # fp32 first-rows buffers (bf16, masked)
+    need += B * T0 * 3 * D * 4 + 3 * B * R * D * 4
     assert need <= n <= need + 16 * 256
+    st, n_none = _ws(mask="none")
+    assert st == bd.IHA_OK and n_none < need - B * T0 * 3 * D * 4
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -85,7 +89,7 @@ def test_forward_rejects_before_any_launch():
     assert st == bd.STATUS_NAMES.index("IHA_ERR_EMPTY_ROW")
     st = lib.iha_attention(1, 64, 2, 128, 0, 0, -1.0, fake, fake, fake, fake, 0, None, None)
     assert st == bd.STATUS_NAMES.index("IHA_ERR_INVALID_ARG")
-    evs = (ctypes.c_void_p * 5)()
+    evs = (ctypes.c_void_p * 6)()
     st = lib.iha_forward_timed(ctypes.byref(p), *args[:8], fake, fake, ctypes.c_size_t(1 << 40),
                                None, evs)
     assert st == bd.STATUS_NAMES.index("IHA_ERR_INVALID_ARG")   # null events
