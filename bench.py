@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Throughput of the IHA forward pass on one MI355X.
 
-A step is one whole forward (mixing fold + input conversion, projection GEMM, attention,
-collapse) over one batch of synthetic inputs that are resident in HBM before timing.
+A step is one whole forward (weight transpose, projection GEMMs + mixing, attention,
+first-rows recomputation, collapse) over one batch of synthetic inputs that are resident in
+HBM before timing.
 Prints one JSON line: pseudo-tokens/s for the whole forward, per-kernel times from HIP
 events recorded on the launch stream around every kernel of every timed step, the
 roofline position of the dominant kernel and of attention, and the CPU oracle timed on
@@ -12,10 +13,9 @@ Work per unit (algorithmic, the count the pages' convention gives):
   attention  4 * d flops per visible (query, key) pair: QK^T and AV at 2 flops per
              multiply-add (textbook eq. 5.34), masked pairs and softmax not counted
   projection 6 * D^2 flops per token (three D x D projections, eq. 5.34) plus the
-             mixing, 6 * D * H * P flops per token (Algorithm 1); the folded design
-             executes 6 * P * D^2 per token on the matrix cores
+             mixing, 6 * D * H * P flops per token (Algorithm 1)
   collapse   bytes: P*H*d*4 read + H*d*4 written per token
-  fold       bytes: 3*D^2*2 read + 3*P*D^2*2 written (bf16 W -> fp16 folded W)
+  prep       bytes: 3*D^2*2 read + 3*D^2*2 written (bf16 weight transpose)
 """
 import argparse
 import json
@@ -94,7 +94,7 @@ def main():
     assert bool(torch.isfinite(out).all()), "non-finite output"
 
     ms_step = (t1 - t0) * 1e3 / args.steps
-    names = ["fold", "gemm", "attention", "first_rows", "collapse"]
+    names = ["prep", "proj_mix", "attention", "first_rows", "collapse"]
     kms = {n: float(np.mean([evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)]))
            for k, n in enumerate(names)}
 
@@ -103,9 +103,8 @@ def main():
     pairs = allowed_pairs(L, w.mask, w.window)
     attn_flops = 4.0 * d * B * H * pairs
     proj_flops = 6.0 * B * N * D * D + 6.0 * B * N * D * H * P
-    gemm_exec_flops = 6.0 * B * N * D * P * D
     collapse_bytes = B * N * (P * H * d * 4 + H * d * 4) + H * H * P * 4
-    fold_bytes = 3 * D * D * 2 + 3 * P * D * D * 2 + 3 * H * H * P * 4 + 2 * B * N * D * 2
+    prep_bytes = 3 * D * D * 2 * 2
 
     def roof(kind, work, ms):
         if kind == "mfma":
@@ -116,11 +115,10 @@ def main():
         return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                 "frac": round(a / (PEAK_HBM / 1e9), 4), "traffic": None}
 
-    roofs = {"fold": roof("hbm", fold_bytes, kms["fold"]),
-             "gemm": roof("mfma", proj_flops, kms["gemm"]),
+    roofs = {"prep": roof("hbm", prep_bytes, kms["prep"]),
+             "proj_mix": roof("mfma", proj_flops, kms["proj_mix"]),
              "attention": roof("mfma", attn_flops, kms["attention"]),
              "collapse": roof("hbm", collapse_bytes, kms["collapse"])}
-    first_rows_ms = kms["first_rows"]
     dominant = max(kms, key=kms.get)
     value = B * P * N / (ms_step * 1e-3)
 
@@ -152,7 +150,6 @@ def main():
                           tflops=roofs["attention"]["achieved"]),
         "kernels_ms": {k: round(v, 4) for k, v in kms.items()},
         "kernel_roofline": roofs,
-        "gemm_executed_tflops": round(gemm_exec_flops / (kms["gemm"] * 1e-3) / 1e12, 2),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -35,14 +35,16 @@
  *   R        [H][H*P]  float    column h'*P + j (0-based form of (h'-1)P + j)
  *   X_out    [B][N][D] float    head h in columns [h*d, (h+1)*d)
  *
- * Precision.  IHA_F32: every step in fp32.  IHA_BF16: the mixing is folded
- * into the weights in fp32, the folded weights, the projected Q/K/V and the
- * attention probabilities are stored as fp16 for the matrix cores (fp32
- * accumulation), softmax state and the per-head attention output are fp32,
- * and X_out is fp32.  Under a causal or window mask the first 128 stacked
- * rows of every (b, h) see the fewest keys and have the largest outputs; they
- * are recomputed with fp32 intermediates (exact bf16 projection, fp32 mixing
- * and attention) so that their absolute error matches the other rows'.
+ * Precision.  IHA_F32: every step in fp32 (the mixing is folded into the
+ * weights).  IHA_BF16: the per-head projections run on the bf16 matrix cores
+ * with the exact bf16 inputs and fp32 accumulation, the mixing is applied to
+ * those fp32 projections in fp32, and the mixed Q/K/V and the attention
+ * probabilities are stored as fp16 for the fp16 matrix cores (fp32
+ * accumulation); softmax state, the per-head attention output and X_out are
+ * fp32.  Under a causal or window mask the first 128 stacked rows of every
+ * (b, h) see the fewest keys and have the largest outputs; their attention is
+ * recomputed in fp32 from fp32 copies of their mixed queries, keys and values,
+ * so that their absolute error matches the other rows'.
  *
  * Ownership and streams.  The caller owns every buffer; all device pointers
  * must be on the current HIP device.  The library keeps no state between
@@ -117,11 +119,11 @@ iha_status iha_forward(const iha_problem* prob, const void* X, const void* W_Q, 
                        size_t workspace_bytes, hipStream_t stream);
 
 /* iha_forward that also records events[0..5] on `stream` around its steps:
- * [0] start, [1] after mixing (weight fold and input conversion), [2] after
- * the projection GEMM, [3] after the attention kernel, [4] after the fp32
- * recomputation of the first stacked rows (no work for IHA_F32 or
- * IHA_MASK_NONE), [5] after the collapse.  The events are created by the
- * caller (hipEventCreate) and must not be NULL. */
+ * [0] start, [1] after the weight preparation (bf16: transpose; fp32: mixing
+ * folded into the weights), [2] after the projections and the mixing, [3]
+ * after the attention kernel, [4] after the fp32 recomputation of the first
+ * stacked rows (no work for IHA_F32 or IHA_MASK_NONE), [5] after the collapse.
+ * The events are created by the caller (hipEventCreate) and must not be NULL. */
 iha_status iha_forward_timed(const iha_problem* prob, const void* X, const void* W_Q,
                              const void* W_K, const void* W_V, const float* alpha_Q,
                              const float* alpha_K, const float* alpha_V, const float* R,

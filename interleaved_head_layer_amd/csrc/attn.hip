@@ -131,26 +131,28 @@ struct RowState {
 constexpr float kRescaleLog2 = 8.f;
 
 // One key tile for one wave: S^T = K Q^T, (masked) online softmax, O^T += V^T P^T.
-template <int DH, int MASK, bool EDGE>
-__device__ __forceinline__ void attn_tile(const half_t* __restrict__ ks, const half_t* __restrict__ vs,
+template <int DH, int MASK>
+__device__ __forceinline__ void attn_tile(bool edge, const half_t* __restrict__ ks, const half_t* __restrict__ vs,
                                           const half8 (&qf)[DH / 16], RowState<DH / 32>& st,
                                           int k0, int qrow, int L, int window, float scale,
                                           float thr, int krow, int l32, int hf) {
   constexpr int KLD = AttnSmem<DH>::KLD, VLD = AttnSmem<DH>::VLD;
   constexpr int NKS = DH / 16, NCB = DH / 32;
+  // The first product of each chain takes the constant 0 as accumulator (no zeroing).
+  const floatx16 zero16 = {};
   floatx16 s[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
     for (int kstep = 0; kstep < NKS; ++kstep) {
       const int kr_ = kb * 32 + krow;
       const half8 kf = *reinterpret_cast<const half8*>(&ks[kr_ * KLD + ((kstep * 2 + hf) ^ kswz<DH>(kr_)) * 8]);
-      s[kb] = mfma32(kf, qf[kstep], s[kb]);
+      s[kb] = mfma32(kf, qf[kstep], kstep == 0 ? zero16 : s[kb]);
     }
   }
-  if (EDGE) {
+  // One tile body for all tiles (two bodies would keep two copies of the O registers);
+  // the key test runs only on tiles that cross a mask edge or the sequence end.
+  if (__builtin_expect(edge, false)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -162,7 +164,10 @@ __device__ __forceinline__ void attn_tile(const half_t* __restrict__ ks, const h
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  {  // maximum with lane l^32 (the other half of this query's keys) via the VALU lane swap
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(fmaxf(mx, __uint_as_float(sw[0])), __uint_as_float(sw[1]));
+  }
   // A row moves its maximum only when a score exceeds it by more than 2^8 (or at its first
   // visible key).  The decision is per row (alpha = 1 exactly for the others), so a row's
   // result never depends on the other rows of the wave.
@@ -272,10 +277,7 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
     bool edge = (k0 + ABN > L);
     if (MASK != kMaskNone) edge |= (k0 + ABN - 1 > q0);
     if (MASK == kMaskWindow) edge |= (k0 <= q0 + ABM - 1 - window);
-    if (edge)
-      attn_tile<DH, MASK, true>(sm.k[stage], sm.v[stage], qf, st, k0, qrow, L, window, scale, thr, krow, l32, hf);
-    else
-      attn_tile<DH, MASK, false>(sm.k[stage], sm.v[stage], qf, st, k0, qrow, L, window, scale, thr, krow, l32, hf);
+    attn_tile<DH, MASK>(edge, sm.k[stage], sm.v[stage], qf, st, k0, qrow, L, window, scale, thr, krow, l32, hf);
     if (more) cp.commit(sm.k[stage ^ 1], sm.v[stage ^ 1]);
     wait_global_loads();
     __syncthreads();

@@ -1,7 +1,8 @@
-// Step 1 of Algorithm 1 ("Interleaved Head Attention" page, section 4): pseudo-head
-// mixing.  Since Q~_{h,j} = sum_m alpha_{m,h,j} X W^(m) = X (sum_m alpha_{m,h,j} W^(m)),
-// the mixing is applied once to the weights (fp32 arithmetic) and the projection
-// becomes one plain GEMM against the folded weights.
+// Step 1 of Algorithm 1 ("Interleaved Head Attention" page, section 4) for fp32 inputs:
+// pseudo-head mixing.  Since Q~_{h,j} = sum_m alpha_{m,h,j} X W^(m) = X (sum_m alpha_{m,h,j} W^(m)),
+// the mixing is applied once to the weights and the projection becomes one plain GEMM
+// against the folded weights.  (bf16 inputs take the unfolded path in proj.hip.)
+// Also: the device flag word helpers.
 //
 // Folded weight layout: Wt[col][k], col in [0, 3*P*H*d), k in [0, D) contiguous
 // (both GEMM operands then carry the contraction index contiguously).
@@ -23,14 +24,10 @@ constexpr int kFoldThreads = kFoldK * kFoldC;
 template <typename Tin>
 __device__ __forceinline__ float load_w(const Tin* p);
 template <>
-__device__ __forceinline__ float load_w<uint16_t>(const uint16_t* p) { return bf16_to_float(*p); }
-template <>
 __device__ __forceinline__ float load_w<float>(const float* p) { return *p; }
 
 template <typename Tout>
 __device__ __forceinline__ Tout store_cvt(float v);
-template <>
-__device__ __forceinline__ half_t store_cvt<half_t>(float v) { return static_cast<half_t>(v); }
 template <>
 __device__ __forceinline__ float store_cvt<float>(float v) { return v; }
 
@@ -82,28 +79,6 @@ __global__ __launch_bounds__(kFoldThreads) void fold_kernel(FoldArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void cvt_bf16_f16_kernel(const uint4* __restrict__ x,
-                                                           uint4* __restrict__ y, int64_t n8) {
-  for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < n8; i += static_cast<int64_t>(gridDim.x) * 256) {
-    const uint4 v = x[i];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const half_t lo = static_cast<half_t>(__uint_as_float(w[q] << 16));
-      const half_t hi = static_cast<half_t>(__uint_as_float(w[q] & 0xFFFF0000u));
-      o[q] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
-             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
-    }
-    y[i] = make_uint4(o[0], o[1], o[2], o[3]);
-  }
-}
-
-__global__ void cvt_tail_kernel(const uint16_t* x, half_t* y, int64_t start, int64_t n) {
-  const int64_t i = start + blockIdx.x * 64LL + threadIdx.x;
-  if (i < n) y[i] = static_cast<half_t>(bf16_to_float(x[i]));
-}
-
 __global__ void clear_flag_kernel(unsigned* flag) { *flag = 0u; }
 
 __global__ __launch_bounds__(256) void check_finite_kernel(const float* __restrict__ x, int64_t n,
@@ -124,26 +99,8 @@ hipError_t launch_fold_impl(const FoldArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_fold_bf16(const FoldArgs& a, hipStream_t s) {
-  return launch_fold_impl<uint16_t, half_t>(a, s);
-}
 hipError_t launch_fold_f32(const FoldArgs& a, hipStream_t s) {
   return launch_fold_impl<float, float>(a, s);
-}
-
-hipError_t launch_cvt_bf16_f16(const uint16_t* x, void* y, int64_t n, hipStream_t s) {
-  const int64_t n8 = n / 8;
-  if (n8 > 0) {
-    const int64_t blocks = std::min<int64_t>((n8 + 255) / 256, 256 * 16);
-    hipLaunchKernelGGL(cvt_bf16_f16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
-                       reinterpret_cast<const uint4*>(x), static_cast<uint4*>(y), n8);
-  }
-  if (n8 * 8 < n) {
-    const int64_t rest = n - n8 * 8;
-    hipLaunchKernelGGL(cvt_tail_kernel, dim3(static_cast<unsigned>((rest + 63) / 64)), dim3(64), 0,
-                       s, x, static_cast<half_t*>(y), n8 * 8, n);
-  }
-  return hipGetLastError();
 }
 
 hipError_t launch_clear_flag(unsigned* flag, hipStream_t s) {

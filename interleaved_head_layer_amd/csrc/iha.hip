@@ -21,8 +21,8 @@ constexpr int64_t kMaxElems = int64_t(1) << 40;  // elements of any one tensor
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t flag, xh, wt, q, k, vt, pbar, ye, qe, ke, vte, total;
-  int T0, R;  // precise first rows: tokens and stacked rows (0 when unused)
+  size_t flag, wt, yqk, yvt, q, k, vt, pbar, qe, ke, vte, total;
+  int R;  // precise first stacked rows (0 when unused)
 };
 
 bool d_supported(int32_t dtype, int64_t d) {
@@ -39,6 +39,11 @@ iha_status validate(const iha_problem* p) {
   if (p->D % p->H != 0) return IHA_ERR_SHAPE;
   if (p->H > kMaxH || p->H * p->H * p->P > 16384) return IHA_ERR_UNSUPPORTED;
   if (!d_supported(p->dtype, p->D / p->H)) return IHA_ERR_UNSUPPORTED;
+  if (p->dtype == IHA_BF16) {
+    // mixing kernels stage alpha as [H][P][Hmax] floats in 64 KB of LDS
+    const int64_t hmax = p->H <= 4 ? 4 : p->H <= 8 ? 8 : p->H <= 16 ? 16 : p->H <= 20 ? 20 : p->H <= 32 ? 32 : 64;
+    if (p->H * p->P * hmax > 16384) return IHA_ERR_UNSUPPORTED;
+  }
   if (p->B * p->N > kMaxRows || p->P * p->N > kMaxRows || p->P > kMaxRows) return IHA_ERR_SHAPE;
   if (p->B * p->N * p->P * p->D > kMaxElems / 4 || 3 * p->P * p->D * p->D > kMaxElems / 4)
     return IHA_ERR_SHAPE;
@@ -51,8 +56,8 @@ iha_status validate(const iha_problem* p) {
 Layout layout_of(const iha_problem& p) {
   const size_t e = p.dtype == IHA_BF16 ? 2 : 4;
   const size_t d = static_cast<size_t>(p.D / p.H);
-  const size_t rows = static_cast<size_t>(p.B) * p.P * p.N;  // stacked rows over the batch
-  const size_t act = rows * p.H * d;                         // elements of Q~, K~, V~, P-bar
+  const size_t M = static_cast<size_t>(p.B) * p.N;          // tokens over the batch
+  const size_t act = M * p.P * p.H * d;                      // elements of Q~, K~, V~, P-bar
   Layout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -61,19 +66,22 @@ Layout layout_of(const iha_problem& p) {
     return o;
   };
   L.flag = take(kAlign);
-  L.xh = p.dtype == IHA_BF16 ? take(static_cast<size_t>(p.B) * p.N * p.D * 2) : 0;
-  L.wt = take(3 * static_cast<size_t>(p.P) * p.D * p.D * e);
+  if (p.dtype == IHA_BF16) {
+    // transposed weights, fp32 projections (token-major Q|K, channel-major V)
+    L.wt = take(3 * static_cast<size_t>(p.D) * p.D * 2);
+    L.yqk = take(M * 2 * p.D * 4);
+    L.yvt = take(M * p.D * 4);
+  } else {
+    L.wt = take(3 * static_cast<size_t>(p.P) * p.D * p.D * 4);  // folded weights
+  }
   L.q = take(act * e);
   L.k = take(act * e);
   L.vt = take(act * e);
   L.pbar = take(act * 4);
-  // bf16 inputs under a causal or window mask: fp32 recomputation of the first rows.
+  // bf16 inputs under a causal or window mask: fp32 copies of the first rows.
   if (p.dtype == IHA_BF16 && p.mask != IHA_MASK_NONE) {
     const int64_t R = std::min<int64_t>(iha::kPreciseRows, p.P * p.N);
-    const int64_t T0 = std::min<int64_t>(p.N, (R + p.P - 1) / p.P);
     L.R = static_cast<int>(R);
-    L.T0 = static_cast<int>(T0);
-    L.ye = take(static_cast<size_t>(p.B) * T0 * 3 * p.D * 4);
     L.qe = take(static_cast<size_t>(p.B) * R * p.D * 4);
     L.ke = take(static_cast<size_t>(p.B) * R * p.D * 4);
     L.vte = take(static_cast<size_t>(p.B) * R * p.D * 4);
@@ -132,43 +140,71 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
                  B, N, D, H, d, P, p.mask, static_cast<long long>(p.window), bf16 ? "bf16" : "f32");
 
   if (ev) IHA_HIP(hipEventRecord(ev[0], stream));
-  // Step 1: mixing folded into the weights; bf16 X converted for the fp16 matrix cores.
-  iha::FoldArgs fa{};
-  fa.W[0] = W_Q;
-  fa.W[1] = W_K;
-  fa.W[2] = W_V;
-  fa.alpha[0] = alpha_Q;
-  fa.alpha[1] = alpha_K;
-  fa.alpha[2] = alpha_V;
-  fa.out_scale[0] = fa.out_scale[1] = fa.out_scale[2] = 1.f;
-  fa.Wt = ws + lay.wt;
-  fa.flag = flag;
-  fa.D = D;
-  fa.H = H;
-  fa.d = d;
-  fa.P = P;
-  IHA_HIP(bf16 ? iha::launch_fold_bf16(fa, stream) : iha::launch_fold_f32(fa, stream));
-  if (bf16)
-    IHA_HIP(iha::launch_cvt_bf16_f16(static_cast<const uint16_t*>(X), ws + lay.xh,
-                                     static_cast<int64_t>(B) * N * D, stream));
-  if (ev) IHA_HIP(hipEventRecord(ev[1], stream));
-
-  // Step 2: projection GEMM into the stacked layouts.
-  iha::GemmArgs g{};
-  g.A = bf16 ? static_cast<const void*>(ws + lay.xh) : X;
-  g.Bt = ws + lay.wt;
-  g.Q = ws + lay.q;
-  g.K = ws + lay.k;
-  g.Vt = ws + lay.vt;
-  g.M = B * N;
-  g.Kdim = D;
-  g.Ncol = 3 * P * H * d;
-  g.PHd = P * H * d;
-  g.Ntok = N;
-  g.P = P;
-  g.H = H;
-  g.d = d;
-  IHA_HIP(bf16 ? iha::launch_gemm_f16(g, stream) : iha::launch_gemm_f32(g, stream));
+  if (bf16) {
+    // Steps 1-2: exact bf16 projections (fp32 accumulation), fp32 mixing into the stacked
+    // fp16 layouts (and fp32 copies of the first rows).
+    iha::ProjArgs pa{};
+    pa.X = static_cast<const uint16_t*>(X);
+    pa.W[0] = static_cast<const uint16_t*>(W_Q);
+    pa.W[1] = static_cast<const uint16_t*>(W_K);
+    pa.W[2] = static_cast<const uint16_t*>(W_V);
+    pa.alpha[0] = alpha_Q;
+    pa.alpha[1] = alpha_K;
+    pa.alpha[2] = alpha_V;
+    pa.Wt = reinterpret_cast<uint16_t*>(ws + lay.wt);
+    pa.Yqk = reinterpret_cast<float*>(ws + lay.yqk);
+    pa.Yvt = reinterpret_cast<float*>(ws + lay.yvt);
+    pa.Q = reinterpret_cast<iha::half_t*>(ws + lay.q);
+    pa.K = reinterpret_cast<iha::half_t*>(ws + lay.k);
+    pa.Vt = reinterpret_cast<iha::half_t*>(ws + lay.vt);
+    if (lay.R > 0) {
+      pa.Qe = reinterpret_cast<float*>(ws + lay.qe);
+      pa.Ke = reinterpret_cast<float*>(ws + lay.ke);
+      pa.Vte = reinterpret_cast<float*>(ws + lay.vte);
+    }
+    pa.B = B;
+    pa.N = N;
+    pa.D = D;
+    pa.H = H;
+    pa.d = d;
+    pa.P = P;
+    pa.R = lay.R;
+    IHA_HIP(iha::launch_clear_flag(flag, stream));
+    IHA_HIP(iha::launch_proj_bf16(pa, stream, ev ? ev[1] : nullptr));
+  } else {
+    // Step 1: mixing folded into the weights (fp32); step 2: fp32 projection GEMM.
+    iha::FoldArgs fa{};
+    fa.W[0] = W_Q;
+    fa.W[1] = W_K;
+    fa.W[2] = W_V;
+    fa.alpha[0] = alpha_Q;
+    fa.alpha[1] = alpha_K;
+    fa.alpha[2] = alpha_V;
+    fa.out_scale[0] = fa.out_scale[1] = fa.out_scale[2] = 1.f;
+    fa.Wt = ws + lay.wt;
+    fa.flag = flag;
+    fa.D = D;
+    fa.H = H;
+    fa.d = d;
+    fa.P = P;
+    IHA_HIP(iha::launch_fold_f32(fa, stream));
+    if (ev) IHA_HIP(hipEventRecord(ev[1], stream));
+    iha::GemmArgs g{};
+    g.A = X;
+    g.Bt = ws + lay.wt;
+    g.Q = ws + lay.q;
+    g.K = ws + lay.k;
+    g.Vt = ws + lay.vt;
+    g.M = B * N;
+    g.Kdim = D;
+    g.Ncol = 3 * P * H * d;
+    g.PHd = P * H * d;
+    g.Ntok = N;
+    g.P = P;
+    g.H = H;
+    g.d = d;
+    IHA_HIP(iha::launch_gemm_f32(g, stream));
+  }
   if (ev) IHA_HIP(hipEventRecord(ev[2], stream));
 
   // Step 3: per-head masked attention over the P*N stacked rows.
@@ -192,26 +228,14 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
   if (lay.R > 0) {
     // The first stacked rows again, with fp32 intermediates (their outputs are the largest).
     iha::EarlyArgs ea{};
-    ea.X = static_cast<const uint16_t*>(X);
-    ea.W[0] = static_cast<const uint16_t*>(W_Q);
-    ea.W[1] = static_cast<const uint16_t*>(W_K);
-    ea.W[2] = static_cast<const uint16_t*>(W_V);
-    ea.alpha[0] = alpha_Q;
-    ea.alpha[1] = alpha_K;
-    ea.alpha[2] = alpha_V;
-    ea.Y = reinterpret_cast<float*>(ws + lay.ye);
     ea.Qe = reinterpret_cast<float*>(ws + lay.qe);
     ea.Ke = reinterpret_cast<float*>(ws + lay.ke);
     ea.Vte = reinterpret_cast<float*>(ws + lay.vte);
     ea.B = B;
-    ea.N = N;
-    ea.D = D;
     ea.H = H;
+    ea.D = D;
     ea.d = d;
-    ea.P = P;
-    ea.T0 = lay.T0;
     ea.R = lay.R;
-    IHA_HIP(iha::launch_early_qkv(ea, stream));
     IHA_HIP(iha::launch_early_attn(ea, at.O, static_cast<int64_t>(at.L) * H * d, p.mask,
                                    std::min(at.window, lay.R), at.qk_scale, stream));
   }

@@ -18,11 +18,7 @@ struct FoldArgs {
   unsigned* flag;
   int D, H, d, P;
 };
-hipError_t launch_fold_bf16(const FoldArgs& a, hipStream_t s);  // bf16 W -> fp16 Wt
-hipError_t launch_fold_f32(const FoldArgs& a, hipStream_t s);   // fp32 W -> fp32 Wt
-
-// bf16 -> fp16 copy of X (values of N(0,1)-like inputs are exact in fp16).
-hipError_t launch_cvt_bf16_f16(const uint16_t* x, void* y, int64_t n, hipStream_t s);
+hipError_t launch_fold_f32(const FoldArgs& a, hipStream_t s);   // fp32 W -> fp32 Wt (fp32 inputs)
 
 // Projection GEMM C[M][3*PHd] = X[M][D] * Wt^T, written as
 //   Q, K : [B][P*N][H][d] (stacked row t*P + j),  Vt : [B][H][d][P*N].
@@ -34,7 +30,6 @@ struct GemmArgs {
   void* Vt;
   int M, Kdim, Ncol, PHd, Ntok, P, H, d;
 };
-hipError_t launch_gemm_f16(const GemmArgs& g, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s);
 
 // Masked attention over the stacked sequence: O = softmax_2(s) V with base-2 scores
@@ -52,20 +47,40 @@ struct AttnArgs {
 hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
 
-// Full-precision recomputation of the first R stacked rows (R = min(128, P*N)) of every
-// (b, h) for bf16 inputs: exact bf16 projection of the first T0 = ceil(R/P) tokens
-// (fp32 accumulation), fp32 mixing into Qe, Ke [B][R][H][d] and Vte [B][H][d][R].
-struct EarlyArgs {
-  const uint16_t* X;      // [B][N][D] bf16
-  const uint16_t* W[3];   // [D][D] bf16
+// bf16 projection path: exact bf16 GEMMs (fp32 accumulation) then fp32 mixing.
+struct NtArgs {
+  const uint16_t* A;  // [I][K] bf16
+  const uint16_t* B;  // [J][K] bf16
+  float* C;           // [I][ldc] fp32
+  int I, J, K;
+  int64_t ldc;
+};
+struct ProjArgs {
+  const uint16_t* X;      // [B*N][D] bf16
+  const uint16_t* W[3];   // [D][D] bf16 (Q, K, V)
   const float* alpha[3];  // [H][H][P]
-  float* Y;               // [B*T0][3*D]
-  float* Qe;
+  uint16_t* Wt;           // [3D][D] bf16 scratch
+  float* Yqk;             // [B*N][2D] fp32 scratch
+  float* Yvt;             // [D][B*N] fp32 scratch
+  half_t* Q;              // [B][P*N][H][d] fp16
+  half_t* K;
+  half_t* Vt;             // [B][H][d][P*N] fp16
+  float* Qe;              // fp32 copies of the first R stacked rows (or null)
   float* Ke;
   float* Vte;
-  int B, N, D, H, d, P, T0, R;
+  int B, N, D, H, d, P, R;
 };
-hipError_t launch_early_qkv(const EarlyArgs& e, hipStream_t s);
+// ev_prep (may be null) is recorded after the weight transpose.
+hipError_t launch_proj_bf16(const ProjArgs& pa, hipStream_t s, hipEvent_t ev_prep);
+
+// fp32 copies of the first R stacked rows (R = min(128, P*N)) of every (b, h) for bf16
+// inputs under a causal or window mask: Qe, Ke [B][R][H][d], Vte [B][H][d][R].
+struct EarlyArgs {
+  const float* Qe;
+  const float* Ke;
+  const float* Vte;
+  int B, H, D, d, R;
+};
 // fp32 attention of those rows (causal / window), written into O rows < R
 // (O [B][L][H][d] with batch stride o_bstride).
 hipError_t launch_early_attn(const EarlyArgs& e, float* O, int64_t o_bstride, int mask, int window,

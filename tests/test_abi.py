@@ -43,13 +43,14 @@ def test_workspace_size_covers_the_intermediates():
     st, n = _ws()
     assert st == bd.IHA_OK
     B, N, D, P = 2, 100, 256, 2
-    rows = B * N * P
-    need = B * N * D * 2 + 3 * P * D * D * 2 + 3 * rows * D * 2 + rows * D * 4
-    R, T0 = min(128, P * N), min(N, -(-128 // P))     # fp32 first-rows buffers (bf16, masked)
-    need += B * T0 * 3 * D * 4 + 3 * B * R * D * 4
+    M, rows = B * N, B * N * P
+    need = 3 * D * D * 2 + M * 2 * D * 4 + M * D * 4      # transposed W, fp32 projections
+    need += 3 * rows * D * 2 + rows * D * 4                # Q~, K~, V~^T (fp16), P-bar (fp32)
+    R = min(128, P * N)                                    # fp32 first rows (bf16, masked)
+    need += 3 * B * R * D * 4
     assert need <= n <= need + 16 * 256
     st, n_none = _ws(mask="none")
-    assert st == bd.IHA_OK and n_none < need - B * T0 * 3 * D * 4
+    assert st == bd.IHA_OK and n_none < need - 3 * B * R * D * 4 + 16 * 256
 
 
 @pytest.mark.parametrize("kw,code", [
