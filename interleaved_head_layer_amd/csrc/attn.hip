@@ -7,7 +7,8 @@
 // Flash-style: the PN x PN score matrix is never formed (the textbook's eq. 5.35 shows
 // why); key tiles stream through LDS and each query row keeps a running maximum and
 // sum (the shift invariance of softmax, textbook section 5.2, makes the rescaling exact).
-// Scores are kept in base 2: s2 = (q . k) * log2(e)/sqrt(d), p = exp2(s2 - max).
+// Scores are kept in base 2: s2 = (q . k) * log2(e)/sqrt(d), p = exp2(s2 - max).  The factor
+// is applied to Q as it is loaded (a caller that stored Q pre-scaled passes 1, which is exact).
 //
 // A valid query always sees itself (window >= 1 is checked on the host), so its sum is
 // at least 1; a row whose sum is zero is reported through the flag word, never divided.
@@ -31,6 +32,7 @@ namespace {
 constexpr int ABM = 128;
 constexpr int ABN = 64;
 constexpr int AThreads = 256;
+constexpr int AWaves = AThreads / 64;
 
 __device__ __forceinline__ int sigma_row(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
 
@@ -62,35 +64,64 @@ __device__ __forceinline__ int kswz(int r) {
 // V^T rows (64 keys = 128 bytes, two rows per 256-byte bank line): chunk c at c ^ ((r >> 1) & 7).
 __device__ __forceinline__ int vswz(int r) { return (r >> 1) & 7; }
 
-// Copy key tile [k0, k0 + 64) into one stage.  DIRECT: global -> LDS loads (no registers;
-// needs L % 8 == 0); otherwise through registers.  Keys past the end load a clamped valid row
-// and are masked out by the caller, so every value in LDS is finite.
+// Copy key tile [k0, k0 + 64) into one stage.  DIRECT: buffer loads straight into LDS (no
+// registers; needs L % 8 == 0).  Each lane keeps two 32-bit K offsets (the K swizzle takes
+// two values over the rounds) and one V offset; the per-round part is a scalar offset.
+// Keys past the end read zero (K rows) or a neighbouring channel row (V^T); both are masked
+// out by the caller, so every value in LDS is finite.  Otherwise through registers.
 template <int DH, bool DIRECT>
 struct TileCopy {
   static constexpr int KCH = DH / 8;                  // 16-byte chunks per K row
-  static constexpr int ROUNDS = DH / 32;              // (64 * DH * 2 bytes) / (256 lanes * 16 bytes)
+  static constexpr int ROUNDS = DH * ABN * 2 / (AThreads * 16);
+  static constexpr int KRB = AWaves * 64 / KCH;       // K rows per round
+  static constexpr int VRB = AWaves * 64 / (ABN / 8); // V^T rows per round
   uint4 kr[DIRECT ? 1 : ROUNDS], vr[DIRECT ? 1 : ROUNDS];
+  __amdgpu_buffer_rsrc_t krs, vrs;
+  unsigned koff[2], voff;
+  int64_t rs;
+  int L;
+
+  __device__ __forceinline__ void init(const half_t* Kb, const half_t* Vb, int64_t rs_, int L_, int h) {
+    rs = rs_;
+    L = L_;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    if (DIRECT) {
+      krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(Kb), static_cast<short>(0),
+                                              static_cast<int>((L_ * rs_ - static_cast<int64_t>(h) * DH) * 2), 0x00020000);
+      vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(Vb), static_cast<short>(0),
+                                              static_cast<int>(static_cast<int64_t>(DH) * L_ * 2), 0x00020000);
+      const int rl = (w * 64 + lane) / KCH, pos = (w * 64 + lane) % KCH;
+#pragma unroll
+      for (int bit = 0; bit < 2; ++bit) {
+        const int sw = (rl & 7) | ((DH == 128 ? bit : 0) << 3);
+        koff[bit] = static_cast<unsigned>((rl * rs_ + (pos ^ sw) * 8) * 2);
+      }
+      const int cl = (w * 64 + lane) / (ABN / 8), vpos = (w * 64 + lane) % (ABN / 8);
+      voff = static_cast<unsigned>((static_cast<int64_t>(cl) * L_ + (vpos ^ vswz(cl)) * 8) * 2);
+    }
+  }
 
   __device__ __forceinline__ void issue(const half_t* __restrict__ Kb, const half_t* __restrict__ Vb,
-                                        int64_t rs, int L, int k0, half_t* kst, half_t* vst) {
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+                                        int k0, half_t* kst, half_t* vst) {
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
 #pragma unroll
     for (int p = 0; p < ROUNDS; ++p) {
-      // K: 16-byte slot (p*4 + w)*64 + lane of the stage -> row r, position pos.
-      const int slot = (p * 4 + w) * 64 + lane;
-      const int r = slot / KCH, pos = slot % KCH;
-      const int key = min(k0 + r, L - 1);
-      const half_t* ksrc = Kb + key * rs + (pos ^ kswz<DH>(r)) * 8;
-      // V^T: slot -> channel row cr (8 slots of 8 keys per row), position vpos.
-      const int cr = slot / (ABN / 8), vpos = slot % (ABN / 8);
-      int vkey = k0 + (vpos ^ vswz(cr)) * 8;
       if (DIRECT) {
-        vkey = min(vkey, L - 8);
-        const half_t* vsrc = Vb + static_cast<int64_t>(cr) * L + vkey;
-        __builtin_amdgcn_global_load_lds(ksrc, (__attribute__((address_space(3))) void*)(kst + (p * 4 + w) * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vsrc, (__attribute__((address_space(3))) void*)(vst + (p * 4 + w) * 512), 16, 0, 0);
+        // K row p*KRB + rl: swizzle bit 3 is bit 4 of the row, i.e. (p*KRB >> 4) & 1.
+        const int bit = ((p * KRB) >> 4) & 1;
+        const unsigned ks_off = static_cast<unsigned>((k0 + p * KRB) * rs * 2);
+        const unsigned vs_off = static_cast<unsigned>((static_cast<int64_t>(p) * VRB * L + k0) * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)(kst + (p * AWaves + w) * 512),
+                                                 16, koff[bit], ks_off, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)(vst + (p * AWaves + w) * 512),
+                                                 16, voff, vs_off, 0, 0);
       } else {
-        kr[p] = *reinterpret_cast<const uint4*>(ksrc);
+        const int slot = (p * AWaves + w) * 64 + lane;
+        const int r = slot / KCH, pos = slot % KCH;
+        const int key = min(k0 + r, L - 1);
+        kr[p] = *reinterpret_cast<const uint4*>(Kb + key * rs + (pos ^ kswz<DH>(r)) * 8);
+        const int cr = slot / (ABN / 8), vpos = slot % (ABN / 8);
+        const int vkey = k0 + (vpos ^ vswz(cr)) * 8;
         const half_t* vsrc = Vb + static_cast<int64_t>(cr) * L + vkey;
         uint16_t e[8];
 #pragma unroll
@@ -107,7 +138,7 @@ struct TileCopy {
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
 #pragma unroll
     for (int p = 0; p < ROUNDS; ++p) {
-      const int slot = (p * 4 + w) * 64 + lane;
+      const int slot = (p * AWaves + w) * 64 + lane;
       *reinterpret_cast<uint4*>(kst + slot * 8) = kr[p];
       *reinterpret_cast<uint4*>(vst + slot * 8) = vr[p];
     }
@@ -119,7 +150,7 @@ __device__ __forceinline__ void wait_global_loads() { asm volatile("s_waitcnt vm
 // Running softmax state of one lane (one query row, shared with lane l^32).
 template <int NCB>
 struct RowState {
-  float m;          // stale running maximum of the raw scores q.k (-inf before any visible key)
+  float m;          // stale running maximum of the base-2 scores (-inf before any visible key)
   float l;          // this lane's share of the running sum
   floatx16 o[NCB];  // O^T accumulators
 };
@@ -130,16 +161,16 @@ struct RowState {
 // makes any such choice of the subtracted maximum exact.
 constexpr float kRescaleLog2 = 8.f;
 
-// One key tile for one wave: S^T = K Q^T, (masked) online softmax, O^T += V^T P^T.
+// One key tile for one wave.  Q is pre-scaled by log2(e)/sqrt(d), so scores are in base 2;
+// the score product starts from the accumulator -m (the row's running maximum), so its
+// output is already s - m and feeds exp2 directly.
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 template <int DH, int MASK>
 __device__ __forceinline__ void attn_tile(bool edge, const half_t* __restrict__ ks, const half_t* __restrict__ vs,
-                                          const half8 (&qf)[DH / 16], RowState<DH / 32>& st,
-                                          int k0, int qrow, int L, int window, float scale,
-                                          float thr, int krow, int l32, int hf) {
+                                          const half8 (&qf)[DH / 16], RowState<DH / 32>& st, floatx16& negm,
+                                          int k0, int qrow, int L, int window, int krow, int l32, int hf) {
   constexpr int KLD = AttnSmem<DH>::KLD, VLD = AttnSmem<DH>::VLD;
   constexpr int NKS = DH / 16, NCB = DH / 32;
-  // The first product of each chain takes the constant 0 as accumulator (no zeroing).
-  const floatx16 zero16 = {};
   floatx16 s[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -147,11 +178,9 @@ __device__ __forceinline__ void attn_tile(bool edge, const half_t* __restrict__ 
     for (int kstep = 0; kstep < NKS; ++kstep) {
       const int kr_ = kb * 32 + krow;
       const half8 kf = *reinterpret_cast<const half8*>(&ks[kr_ * KLD + ((kstep * 2 + hf) ^ kswz<DH>(kr_)) * 8]);
-      s[kb] = mfma32(kf, qf[kstep], kstep == 0 ? zero16 : s[kb]);
+      s[kb] = mfma32(kf, qf[kstep], kstep == 0 ? negm : s[kb]);
     }
   }
-  // One tile body for all tiles (two bodies would keep two copies of the O registers);
-  // the key test runs only on tiles that cross a mask edge or the sequence end.
   if (__builtin_expect(edge, false)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -164,36 +193,49 @@ __device__ __forceinline__ void attn_tile(bool edge, const half_t* __restrict__ 
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-  {  // maximum with lane l^32 (the other half of this query's keys) via the VALU lane swap
+  {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
     mx = fmaxf(fmaxf(mx, __uint_as_float(sw[0])), __uint_as_float(sw[1]));
   }
-  // A row moves its maximum only when a score exceeds it by more than 2^8 (or at its first
-  // visible key).  The decision is per row (alpha = 1 exactly for the others), so a row's
-  // result never depends on the other rows of the wave.
-  const bool need = mx > st.m + thr;
-  if (__any(need)) {
-    const float m_new = need ? mx : st.m;
-    const float alpha = !need ? 1.f : (st.m == -__builtin_inff()) ? 0.f : fast_exp2((st.m - m_new) * scale);
+  // mx is relative to the current offset.  A row moves its maximum at its first visible key
+  // or when a score exceeds it by more than 2^8; the others keep alpha = 1, delta = 0.
+  const bool first = st.m == -__builtin_inff();
+  const bool need = first ? (mx > -__builtin_inff()) : (mx > kRescaleLog2);
+  if (__builtin_expect(__any(need), 0)) {
+    const float delta = need ? mx : 0.f;
+    const float alpha = !need ? 1.f : first ? 0.f : fast_exp2(-mx);
     st.l *= alpha;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st.o[cb][r] *= alpha;
-    st.m = m_new;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] -= delta;
+    if (need) st.m = first ? mx : st.m + mx;
+    const float nm = st.m == -__builtin_inff() ? 0.f : -st.m;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) negm[r] = nm;
   }
-  const float m_off = (st.m == -__builtin_inff()) ? 0.f : st.m * scale;
-  float psum = 0.f;
   half8 pf[2][2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = fast_exp2(fmaf(s[kb][r], scale, -m_off));
-      psum += p;
-      pf[kb][r >> 3][r & 7] = static_cast<half_t>(p);
-    }
-  st.l += psum;
+    for (int r = 0; r < 16; ++r) pf[kb][r >> 3][r & 7] = static_cast<half_t>(fast_exp2(s[kb][r]));
+  // Row sum of the rounded probabilities (the values the V product uses), fp32 accumulate.
+  const half2v ones = {static_cast<half_t>(1.f), static_cast<half_t>(1.f)};
+  float psum = st.l;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const half2v pr = {pf[kb][s2][2 * e], pf[kb][s2][2 * e + 1]};
+        psum = __builtin_amdgcn_fdot2(pr, ones, psum, false);
+      }
+  st.l = psum;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -237,6 +279,9 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
   for (int s = 0; s < NKS; ++s) {
     if (qrow < L) {
       qf[s] = *reinterpret_cast<const half8*>(Qb + qrow * rs + s * 16 + 8 * hf);
+      // Base-2 score scale folded into Q (exact when qk_scale == 1).
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[s][e] = static_cast<half_t>(static_cast<float>(qf[s][e]) * a.qk_scale);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) qf[s][e] = static_cast<half_t>(0.f);
@@ -248,8 +293,9 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
   if (MASK == kMaskWindow) klo = max(0, q0 - window + 1);
   const int kt0 = klo / ABN, kt1 = (khi + ABN - 1) / ABN;
 
-  const float scale = a.qk_scale;
-  const float thr = kRescaleLog2 / scale;
+  floatx16 negm;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negm[r] = 0.f;
   RowState<NCB> st;
   st.m = -__builtin_inff();
   st.l = 0.f;
@@ -259,8 +305,9 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) st.o[cb][r] = 0.f;
 
   TileCopy<DH, DIRECT> cp;
+  cp.init(Kb, Vb, rs, L, h);
   if (kt0 < kt1) {
-    cp.issue(Kb, Vb, rs, L, kt0 * ABN, sm.k[0], sm.v[0]);
+    cp.issue(Kb, Vb, kt0 * ABN, sm.k[0], sm.v[0]);
     cp.commit(sm.k[0], sm.v[0]);
   }
   wait_global_loads();
@@ -272,12 +319,12 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
     const int stage = (kt - kt0) & 1;
     const bool more = kt + 1 < kt1;
     // The other stage was last read before the previous barrier: refill it now.
-    if (more) cp.issue(Kb, Vb, rs, L, k0 + ABN, sm.k[stage ^ 1], sm.v[stage ^ 1]);
+    if (more) cp.issue(Kb, Vb, k0 + ABN, sm.k[stage ^ 1], sm.v[stage ^ 1]);
     // Only tiles that cross a mask edge or the end of the sequence test keys.
     bool edge = (k0 + ABN > L);
     if (MASK != kMaskNone) edge |= (k0 + ABN - 1 > q0);
     if (MASK == kMaskWindow) edge |= (k0 <= q0 + ABM - 1 - window);
-    attn_tile<DH, MASK>(edge, sm.k[stage], sm.v[stage], qf, st, k0, qrow, L, window, scale, thr, krow, l32, hf);
+    attn_tile<DH, MASK>(edge, sm.k[stage], sm.v[stage], qf, st, negm, k0, qrow, L, window, krow, l32, hf);
     if (more) cp.commit(sm.k[stage ^ 1], sm.v[stage ^ 1]);
     wait_global_loads();
     __syncthreads();
@@ -306,6 +353,7 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
       }
   }
 }
+
 
 // ------------------------------------------------------------ fp32 kernel (VALU)
 // One thread per query row; the wave walks the union of its rows' key ranges so that
@@ -365,7 +413,10 @@ template <int DH, int MASK>
 hipError_t launch_f16_impl(const AttnArgs& a, hipStream_t s) {
   const int nqt = (a.L + ABM - 1) / ABM;
   const dim3 grid(nqt * a.H * a.B);
-  if (a.L % 8 == 0)
+  // Buffer loads: 16-byte aligned V^T rows (L % 8 == 0) and 32-bit byte offsets within one
+  // batch's K and one head's V^T.
+  const bool direct = a.L % 8 == 0 && static_cast<int64_t>(a.L) * a.H * DH * 2 < (int64_t{1} << 31);
+  if (direct)
     hipLaunchKernelGGL((attn_fwd_f16_kernel<DH, MASK, true>), grid, dim3(AThreads), 0, s, a);
   else
     hipLaunchKernelGGL((attn_fwd_f16_kernel<DH, MASK, false>), grid, dim3(AThreads), 0, s, a);

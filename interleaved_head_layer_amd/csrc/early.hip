@@ -16,101 +16,150 @@ namespace iha {
 namespace {
 
 // Attention of the first R stacked rows in fp32 (causal or window mask; a row i sees keys
-// i' <= i, so only keys < R are involved).  Block: 16 query rows of one (b, h); the scores
-// of those rows live in LDS, keys and values stream through LDS in chunks of 32.
-// grid: (ceil(R / 16), H, B); block 256.
-constexpr int ERows = 16, EKeys = 32;
+// i' <= i, so only keys < R <= 128 are involved).  Block: 32 query rows of one (b, h),
+// 512 threads; thread t owns row r = t / 16 and lane g = t % 16 of that row's group.
+//   scores:  thread (r, g) computes keys kc0 + g + 16u (u < 8) -> the row's scores sit in
+//            the 16 lanes of its group, so max and sum are 16-lane shuffles;
+//   P V:     thread (r, g) computes channels g + 16u (u < DH / 16).
+// All keys the block needs are staged in LDS at once, then (through the same buffer) all
+// values, whose global loads are issued into registers before the score phase.
+// grid: (ceil(R / 32), H, B).
+constexpr int ERows = 32, EThreads = 512, EGroup = 16;
+constexpr int EStride = kPreciseRows + 4;  // floats per LDS row (float4-aligned, staggered banks)
 
 template <int DH>
-__global__ __launch_bounds__(256) void early_attn_kernel(EarlyArgs e, float* __restrict__ O,
-                                                         int64_t o_bstride, int mask, int window,
-                                                         float scale) {
-  __shared__ float qs[ERows][DH + 1];
-  __shared__ float ks[EKeys][DH + 1];
-  __shared__ float vs[DH][EKeys + 1];
-  __shared__ float ps[ERows][kPreciseRows + 1];
-  __shared__ float inv_l[ERows];
+__global__ __launch_bounds__(EThreads) void early_attn_kernel(EarlyArgs e, float* __restrict__ O,
+                                                              int64_t o_bstride, int mask,
+                                                              int window, float scale) {
+  static_assert(DH + 4 <= EStride, "row stride");
+  __shared__ __attribute__((aligned(16))) float qs[ERows][EStride];  // Q rows, then P rows
+  __shared__ __attribute__((aligned(16))) float kv[kPreciseRows][EStride];  // K[n][c] then V^T[c][n]
   const int R = e.R, H = e.H, D = e.D;
   const int h = blockIdx.y, b = blockIdx.z;
   const int i0 = blockIdx.x * ERows;
   const int tid = threadIdx.x;
+  const int r = tid / EGroup, g = tid % EGroup;
   const float* __restrict__ Qb = e.Qe + static_cast<int64_t>(b) * R * D + h * DH;
   const float* __restrict__ Kb = e.Ke + static_cast<int64_t>(b) * R * D + h * DH;
   const float* __restrict__ Vb = e.Vte + static_cast<int64_t>(b * H + h) * DH * R;
 
-  for (int x = tid; x < ERows * DH; x += 256) {
-    const int r = x / DH, c = x % DH;
-    qs[r][c] = (i0 + r < R) ? Qb[static_cast<int64_t>(i0 + r) * D + c] : 0.f;
-  }
-  const int khi = min(R, i0 + ERows);                        // keys <= the last row
+  const int khi = min(R, i0 + ERows);  // keys <= the block's last row
   const int klo = mask == kMaskWindow ? max(0, i0 - window + 1) : 0;
-  const int kc0 = klo / EKeys * EKeys;
+  const int kc0 = klo & ~3;
+  const int nk = khi - kc0;             // keys staged (<= 128)
+  const int nk4 = (nk + 3) & ~3;        // P V contraction length (zero-padded)
+  const int nu = (nk + EGroup - 1) / EGroup;  // score columns per thread in use
 
-  // Scores s2 = (q . k) * scale for visible pairs, -inf otherwise.
-  for (int kc = kc0; kc < khi; kc += EKeys) {
-    __syncthreads();
-    for (int x = tid; x < EKeys * DH; x += 256) {
-      const int kk = x / DH, c = x % DH;
-      ks[kk][c] = (kc + kk < R) ? Kb[static_cast<int64_t>(kc + kk) * D + c] : 0.f;
-    }
-    __syncthreads();
-    for (int x = tid; x < ERows * EKeys; x += 256) {
-      const int r = x / EKeys, kk = x % EKeys;
-      const int i = i0 + r, k = kc + kk;
-      float dot = 0.f;
-#pragma unroll 8
-      for (int c = 0; c < DH; ++c) dot = fmaf(qs[r][c], ks[kk][c], dot);
-      const bool vis = k < R && k <= i && (mask != kMaskWindow || k > i - window);
-      ps[r][k] = vis ? dot * scale : -__builtin_inff();
-    }
+  // Stage Q (32 rows) and K (nk rows, zero-filled to a multiple of 16) as float4; every
+  // global load of the block (Q, K and the values below) is issued before the first wait.
+  constexpr int C4 = DH / 4;
+  constexpr int QPT = ERows * C4 / EThreads, KPT = kPreciseRows * C4 / EThreads;
+  floatx4 qreg[QPT], kreg[KPT];
+#pragma unroll
+  for (int q = 0; q < QPT; ++q) {
+    const int x = tid + q * EThreads, rr = x / C4, c = (x % C4) * 4;
+    qreg[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (i0 + rr < R) qreg[q] = *reinterpret_cast<const floatx4*>(Qb + static_cast<int64_t>(i0 + rr) * D + c);
+  }
+#pragma unroll
+  for (int q = 0; q < KPT; ++q) {
+    const int x = tid + q * EThreads, n = x / C4, c = (x % C4) * 4;
+    kreg[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (n < nk) kreg[q] = *reinterpret_cast<const floatx4*>(Kb + static_cast<int64_t>(kc0 + n) * D + c);
+  }
+  // Values V^T[c][kc0 + n] for n < nk4 into registers (rows of V^T have stride R, which need
+  // not be a multiple of 4, so these are scalar loads).
+  constexpr int VPT = DH * kPreciseRows / EThreads;
+  float vreg[VPT];
+#pragma unroll
+  for (int q = 0; q < VPT; ++q) {
+    const int x = tid + q * EThreads;
+    const int c = x / kPreciseRows, n = x % kPreciseRows;
+    vreg[q] = (n < nk) ? Vb[static_cast<int64_t>(c) * R + kc0 + n] : 0.f;
+  }
+#pragma unroll
+  for (int q = 0; q < QPT; ++q) {
+    const int x = tid + q * EThreads;
+    *reinterpret_cast<floatx4*>(&qs[x / C4][(x % C4) * 4]) = qreg[q];
+  }
+#pragma unroll
+  for (int q = 0; q < KPT; ++q) {
+    const int x = tid + q * EThreads, n = x / C4;
+    if (n < nu * EGroup) *reinterpret_cast<floatx4*>(&kv[n][(x % C4) * 4]) = kreg[q];
   }
   __syncthreads();
-  // Row softmax over [kc0, khi): 16 threads per row, max and sum combined with shuffles.
-  {
-    const int r = tid / 16, sub = tid % 16;
-    float mx = -__builtin_inff();
-    for (int k = kc0 + sub; k < khi; k += 16) mx = fmaxf(mx, ps[r][k]);
+
+  // Scores of row i0 + r against keys kc0 + g + 16u.
+  float s[kPreciseRows / EGroup];
 #pragma unroll
-    for (int off = 8; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 16));
-    float sum = 0.f;
-    for (int k = kc0 + sub; k < khi; k += 16) {
-      const float p = (mx == -__builtin_inff()) ? 0.f : fast_exp2(ps[r][k] - mx);
-      ps[r][k] = p;
-      sum += p;
-    }
+  for (int u = 0; u < kPreciseRows / EGroup; ++u) s[u] = 0.f;
+#pragma unroll 4
+  for (int c = 0; c < DH; c += 4) {
+    const floatx4 q4 = *reinterpret_cast<const floatx4*>(&qs[r][c]);
 #pragma unroll
-    for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 16);
-    if (sub == 0) inv_l[r] = sum > 0.f ? 1.f / sum : 0.f;
-  }
-  // O[i][c] = sum_k p[i][k] v[k][c] / l[i].
-  constexpr int PER = ERows * DH / 256;
-  float acc[PER];
-#pragma unroll
-  for (int q = 0; q < PER; ++q) acc[q] = 0.f;
-  for (int kc = kc0; kc < khi; kc += EKeys) {
-    __syncthreads();
-    for (int x = tid; x < DH * EKeys; x += 256) {
-      const int c = x / EKeys, kk = x % EKeys;
-      vs[c][kk] = (kc + kk < R) ? Vb[static_cast<int64_t>(c) * R + kc + kk] : 0.f;
-    }
-    __syncthreads();
-    const int kn = min(EKeys, khi - kc);
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int x = tid + 256 * q;
-      const int r = x / DH, c = x % DH;
-      float a = acc[q];
-      for (int kk = 0; kk < kn; ++kk) a = fmaf(ps[r][kc + kk], vs[c][kk], a);
-      acc[q] = a;
+    for (int u = 0; u < kPreciseRows / EGroup; ++u) {
+      if (u < nu) {
+        const floatx4 k4 = *reinterpret_cast<const floatx4*>(&kv[g + EGroup * u][c]);
+        s[u] = fmaf(q4[0], k4[0], s[u]);
+        s[u] = fmaf(q4[1], k4[1], s[u]);
+        s[u] = fmaf(q4[2], k4[2], s[u]);
+        s[u] = fmaf(q4[3], k4[3], s[u]);
+      }
     }
   }
+  const int i = i0 + r;
+  float mx = -__builtin_inff();
 #pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    const int x = tid + 256 * q;
-    const int r = x / DH, c = x % DH;
-    if (i0 + r < R)
-      O[static_cast<int64_t>(b) * o_bstride + static_cast<int64_t>(i0 + r) * D + h * DH + c] =
-          acc[q] * inv_l[r];
+  for (int u = 0; u < kPreciseRows / EGroup; ++u) {
+    const int k = kc0 + g + EGroup * u;
+    const bool vis = u < nu && k < khi && k <= i && (mask != kMaskWindow || k > i - window);
+    s[u] = vis ? s[u] * scale : -__builtin_inff();
+    mx = fmaxf(mx, s[u]);
+  }
+#pragma unroll
+  for (int off = EGroup / 2; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, EGroup));
+  float sum = 0.f;
+#pragma unroll
+  for (int u = 0; u < kPreciseRows / EGroup; ++u) {
+    s[u] = (mx == -__builtin_inff()) ? 0.f : fast_exp2(s[u] - mx);  // exp2(-inf) = 0
+    sum += s[u];
+  }
+#pragma unroll
+  for (int off = EGroup / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, EGroup);
+  const float inv_l = sum > 0.f ? 1.f / sum : 0.f;
+  __syncthreads();  // every thread is done reading Q and K
+
+  // P rows (over the staged key range) into qs, V^T into kv.
+#pragma unroll
+  for (int u = 0; u < kPreciseRows / EGroup; ++u) qs[r][g + EGroup * u] = s[u];
+#pragma unroll
+  for (int q = 0; q < VPT; ++q) {
+    const int x = tid + q * EThreads;
+    kv[x / kPreciseRows][x % kPreciseRows] = vreg[q];
+  }
+  __syncthreads();
+
+  // O[i][c] = sum_n p[i][n] v[n][c] / l[i] for channels c = g + 16u.
+  constexpr int CU = DH / EGroup;
+  float acc[CU];
+#pragma unroll
+  for (int u = 0; u < CU; ++u) acc[u] = 0.f;
+#pragma unroll 2
+  for (int n = 0; n < nk4; n += 4) {
+    const floatx4 p4 = *reinterpret_cast<const floatx4*>(&qs[r][n]);
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      const floatx4 v4 = *reinterpret_cast<const floatx4*>(&kv[g + EGroup * u][n]);
+      acc[u] = fmaf(p4[0], v4[0], acc[u]);
+      acc[u] = fmaf(p4[1], v4[1], acc[u]);
+      acc[u] = fmaf(p4[2], v4[2], acc[u]);
+      acc[u] = fmaf(p4[3], v4[3], acc[u]);
+    }
+  }
+  if (i < R) {
+    float* dst = O + static_cast<int64_t>(b) * o_bstride + static_cast<int64_t>(i) * D + h * DH;
+#pragma unroll
+    for (int u = 0; u < CU; ++u) dst[g + EGroup * u] = acc[u] * inv_l;
   }
 }
 
@@ -120,11 +169,14 @@ __global__ __launch_bounds__(256) void early_attn_kernel(EarlyArgs e, float* __r
 namespace iha {
 hipError_t launch_early_attn(const EarlyArgs& e, float* O, int64_t o_bstride, int mask, int window,
                              float scale, hipStream_t s) {
+  if (e.R <= 0 || e.R > kPreciseRows) return hipErrorInvalidValue;
   const dim3 grid((e.R + ERows - 1) / ERows, e.H, e.B);
   if (e.d == 64)
-    hipLaunchKernelGGL(early_attn_kernel<64>, grid, dim3(256), 0, s, e, O, o_bstride, mask, window, scale);
+    hipLaunchKernelGGL(early_attn_kernel<64>, grid, dim3(EThreads), 0, s, e, O, o_bstride, mask,
+                       window, scale);
   else if (e.d == 128)
-    hipLaunchKernelGGL(early_attn_kernel<128>, grid, dim3(256), 0, s, e, O, o_bstride, mask, window, scale);
+    hipLaunchKernelGGL(early_attn_kernel<128>, grid, dim3(EThreads), 0, s, e, O, o_bstride, mask,
+                       window, scale);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -169,6 +169,7 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
     pa.d = d;
     pa.P = P;
     pa.R = lay.R;
+    pa.qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
     IHA_HIP(iha::launch_clear_flag(flag, stream));
     IHA_HIP(iha::launch_proj_bf16(pa, stream, ev ? ev[1] : nullptr));
   } else {
@@ -222,8 +223,14 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
   at.window = p.mask == IHA_MASK_WINDOW
                   ? static_cast<int>(p.window < at.L ? p.window : static_cast<int64_t>(at.L))
                   : 0;
-  at.qk_scale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
-  IHA_HIP(bf16 ? iha::launch_attn_f16(at, stream) : iha::launch_attn_f32(at, stream));
+  const float score_scale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
+  at.qk_scale = score_scale;
+  if (bf16) {
+    at.qk_scale = 1.f;  // the fp16 Q was stored pre-scaled
+    IHA_HIP(iha::launch_attn_f16(at, stream));
+  } else {
+    IHA_HIP(iha::launch_attn_f32(at, stream));
+  }
   if (ev) IHA_HIP(hipEventRecord(ev[3], stream));
   if (lay.R > 0) {
     // The first stacked rows again, with fp32 intermediates (their outputs are the largest).
@@ -237,7 +244,7 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
     ea.d = d;
     ea.R = lay.R;
     IHA_HIP(iha::launch_early_attn(ea, at.O, static_cast<int64_t>(at.L) * H * d, p.mask,
-                                   std::min(at.window, lay.R), at.qk_scale, stream));
+                                   std::min(at.window, lay.R), score_scale, stream));
   }
   if (ev) IHA_HIP(hipEventRecord(ev[4], stream));
 

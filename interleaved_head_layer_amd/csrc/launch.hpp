@@ -62,13 +62,14 @@ struct ProjArgs {
   uint16_t* Wt;           // [3D][D] bf16 scratch
   float* Yqk;             // [B*N][2D] fp32 scratch
   float* Yvt;             // [D][B*N] fp32 scratch
-  half_t* Q;              // [B][P*N][H][d] fp16
+  half_t* Q;              // [B][P*N][H][d] fp16, multiplied by qscale
   half_t* K;
   half_t* Vt;             // [B][H][d][P*N] fp16
   float* Qe;              // fp32 copies of the first R stacked rows (or null)
   float* Ke;
   float* Vte;
   int B, N, D, H, d, P, R;
+  float qscale;           // factor applied to the fp16 Q (the base-2 score scale)
 };
 // ev_prep (may be null) is recorded after the weight transpose.
 hipError_t launch_proj_bf16(const ProjArgs& pa, hipStream_t s, hipEvent_t ev_prep);

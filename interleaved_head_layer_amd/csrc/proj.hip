@@ -36,74 +36,82 @@ __global__ __launch_bounds__(256) void wprep_kernel(ProjArgs pa) {
 
 // ------------------------------------------------------------------- NT GEMM
 // C[i][j] = sum_k A[i][k] * B[j][k]; A [I][K], B [J][K] bf16 (k contiguous), C fp32 with
-// row stride ldc.  128 x 128 tiles, K slices of 64, 4 waves as 2 x 2 (64 x 64 each).
-// Operand slices go global -> LDS directly into a two-stage ring; 128-byte rows with
-// 16-byte chunks XOR-swizzled by (row >> 1) & 7 so 16 lanes reading 16 rows hit 16
-// bank groups.  Rows past I / J load a clamped valid row; their results are not stored.
-constexpr int GT = 128, GK = 64;
+// row stride ldc; K a multiple of 64.  256 x 256 tiles, 8 waves as 2 x 4 (128 x 64 each:
+// every A fragment read from LDS feeds two matrix-core products, every B fragment four),
+// K slices of 64 in a two-stage LDS ring filled by buffer loads straight into LDS.  Rows
+// are 128 bytes with 16-byte chunks XOR-swizzled by (row >> 1) & 7, so the 16 lanes that
+// read 16 rows of one chunk hit 16 bank groups.  Rows past I / J read zero (buffer range
+// check) and their results are not stored.  The operands must each span < 2 GiB (the
+// launcher splits larger problems).
+constexpr int GTI = 256, GTJ = 256, GK = 64, GWaves = 8, GThreads = GWaves * 64;
 
 __device__ __forceinline__ int gswz(int r) { return (r >> 1) & 7; }
 
 struct NtSmem {
-  uint16_t a[2][GT * GK];
-  uint16_t b[2][GT * GK];
+  uint16_t a[2][GTI * GK];
+  uint16_t b[2][GTJ * GK];
 };
 
-__device__ __forceinline__ void nt_issue(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
-                                         int I, int J, int K, int i0, int j0, int k0, uint16_t* as,
-                                         uint16_t* bs) {
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {  // 128 rows x 128 bytes = 16 KB = 4 rounds of 256 x 16 bytes
-    const int slot = (p * 4 + w) * 64 + lane;
-    const int r = slot / 8, pos = slot % 8;
-    const int c = pos ^ gswz(r);
-    const uint16_t* sa = A + static_cast<int64_t>(min(i0 + r, I - 1)) * K + k0 + c * 8;
-    const uint16_t* sb = B + static_cast<int64_t>(min(j0 + r, J - 1)) * K + k0 + c * 8;
-    __builtin_amdgcn_global_load_lds(sa, (__attribute__((address_space(3))) void*)(as + (p * 4 + w) * 512), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(sb, (__attribute__((address_space(3))) void*)(bs + (p * 4 + w) * 512), 16, 0, 0);
-  }
-}
-
-__global__ __launch_bounds__(256, 2) void gemm_nt_bf16_kernel(NtArgs g) {
+__global__ __launch_bounds__(GThreads, 1) void gemm_nt_bf16_kernel(NtArgs g) {
   __shared__ __attribute__((aligned(16))) NtSmem sm;
-  const uint16_t* __restrict__ A = g.A;
-  const uint16_t* __restrict__ B = g.B;
   const int I = g.I, J = g.J, K = g.K;
-  const int ntj = (J + GT - 1) / GT;
+  const int ntj = (J + GTJ - 1) / GTJ, nti = (I + GTI - 1) / GTI;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  // Groups of 8 row tiles sweep the column tiles, so a group's A slices stay in L2.
-  const int nti = (I + GT - 1) / GT;
-  const int group = lid / (8 * ntj);
-  const int first_i = group * 8;
-  const int gsize = min(8, nti - first_i);
-  const int ti = first_i + (lid % (8 * ntj)) % gsize;
-  const int tj = (lid % (8 * ntj)) / gsize;
-  const int i0 = ti * GT, j0 = tj * GT;
+  // Groups of 4 row tiles sweep the column tiles, so a group's A slices stay in L2.
+  constexpr int GR = 4;
+  const int group = lid / (GR * ntj);
+  const int first_i = group * GR;
+  const int gsize = min(GR, nti - first_i);
+  const int ti = first_i + (lid % (GR * ntj)) % gsize;
+  const int tj = (lid % (GR * ntj)) / gsize;
+  const int i0 = ti * GTI, j0 = tj * GTJ;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
-  const int wm = wave >> 1, wn = wave & 1;
-  floatx16 acc[2][2];
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(g.A), static_cast<short>(0), static_cast<int>(static_cast<int64_t>(I) * K * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(g.B), static_cast<short>(0), static_cast<int>(static_cast<int64_t>(J) * K * 2), 0x00020000);
+  // Copy slot (p * 8 + wave) * 64 + lane of a stage -> row 64p + 8 * wave + lane / 8, chunk
+  // lane % 8; the swizzle depends on the row only through 8 * wave + lane / 8.
+  const int rl = 8 * wave + (lane >> 3), pos = lane & 7;
+  const unsigned loff = static_cast<unsigned>((rl * K + (pos ^ gswz(rl)) * 8) * 2);
+  auto issue = [&](int k0, int st) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int p = 0; p < GTI / 64; ++p)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (__attribute__((address_space(3))) void*)(sm.a[st] + (p * GWaves + wave) * 512), 16, loff,
+          static_cast<unsigned>((static_cast<int64_t>(i0 + 64 * p) * K + k0) * 2), 0, 0);
+#pragma unroll
+    for (int p = 0; p < GTJ / 64; ++p)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, (__attribute__((address_space(3))) void*)(sm.b[st] + (p * GWaves + wave) * 512), 16, loff,
+          static_cast<unsigned>((static_cast<int64_t>(j0 + 64 * p) * K + k0) * 2), 0, 0);
+  };
+
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int nk = K / GK;
-  nt_issue(A, B, I, J, K, i0, j0, 0, sm.a[0], sm.b[0]);
+  issue(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
-    if (kt + 1 < nk) nt_issue(A, B, I, J, K, i0, j0, (kt + 1) * GK, sm.a[st ^ 1], sm.b[st ^ 1]);
+    if (kt + 1 < nk) issue((kt + 1) * GK, st ^ 1);  // the other stage was last read before the barrier
 #pragma unroll
     for (int s = 0; s < GK / 16; ++s) {
-      bf16x8 af[2], bfr[2];
+      bf16x8 af[4], bfr[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = wm * 64 + i * 32 + l32;
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm * 128 + i * 32 + l32;
         af[i] = *reinterpret_cast<const bf16x8*>(&sm.a[st][r * GK + ((s * 2 + hf) ^ gswz(r)) * 8]);
       }
 #pragma unroll
@@ -112,7 +120,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_bf16_kernel(NtArgs g) {
         bfr[j] = *reinterpret_cast<const bf16x8*>(&sm.b[st][r * GK + ((s * 2 + hf) ^ gswz(r)) * 8]);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
@@ -122,22 +130,45 @@ __global__ __launch_bounds__(256, 2) void gemm_nt_bf16_kernel(NtArgs g) {
   }
   // Lane l holds C[8*(r/4) + 4*hf + r%4][l%32] of each 32x32 block.
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int col = j0 + wn * 64 + j * 32 + l32;
       if (col >= J) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = i0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        const int row = i0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
         if (row < I) g.C[static_cast<int64_t>(row) * g.ldc + col] = acc[i][j][r];
       }
     }
 }
 
+// Launch C = A B^T, splitting A's rows or B's rows into chunks whose bytes fit the 32-bit
+// buffer offsets (a chunk is a multiple of the tile height).
+hipError_t launch_gemm_nt(NtArgs g, hipStream_t s) {
+  const int64_t max_rows = ((int64_t{1} << 31) - 1) / (static_cast<int64_t>(g.K) * 2) / GTI * GTI;
+  if (max_rows < GTI) return hipErrorInvalidValue;
+  const NtArgs full = g;
+  for (int64_t i0 = 0; i0 < full.I; i0 += max_rows) {
+    for (int64_t j0 = 0; j0 < full.J; j0 += max_rows) {
+      NtArgs c = full;
+      c.A = full.A + i0 * full.K;
+      c.B = full.B + j0 * full.K;
+      c.C = full.C + i0 * full.ldc + j0;
+      c.I = static_cast<int>(std::min<int64_t>(max_rows, full.I - i0));
+      c.J = static_cast<int>(std::min<int64_t>(max_rows, full.J - j0));
+      const int tiles = ((c.I + GTI - 1) / GTI) * ((c.J + GTJ - 1) / GTJ);
+      hipLaunchKernelGGL(gemm_nt_bf16_kernel, dim3(tiles), dim3(GThreads), 0, s, c);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
 // ------------------------------------------------------------------- mixing
-// One thread owns one (token, channel c): it loads the H source values y_m once and writes
-// all H*P outputs  out[h][j] = sum_m alpha[m][h][j] * y_m  (fp32 arithmetic).  The block
+// A thread loads the H source values y_m of a few (token, channel) pairs once and writes all
+// H*P outputs  out[h][j] = sum_m alpha[m][h][j] * y_m  of each (fp32 arithmetic).  The block
 // first stages alpha transposed to [h][j][m] in LDS, zero-padded to HMAX source heads, so the
 // inner loop is branch-free FMAs on broadcast LDS reads.
 template <int HMAX>
@@ -149,77 +180,147 @@ __device__ __forceinline__ void stage_alpha(const float* __restrict__ alpha, int
   __syncthreads();
 }
 
-template <int HMAX>
-__device__ __forceinline__ float mix_one(const float* as_hj, const float (&ym)[HMAX]) {
-  float acc = 0.f;
+// acc[w] = sum_m alpha[m][h][j] * ym[m][w] for W independent values (channels or tokens).
+template <int HMAX, int W>
+__device__ __forceinline__ void mix_w(const float* as_hj, const float (&ym)[HMAX][W], float (&acc)[W]) {
+#pragma unroll
+  for (int w = 0; w < W; ++w) acc[w] = 0.f;
 #pragma unroll
   for (int m = 0; m < HMAX; m += 4) {
     const floatx4 a4 = *reinterpret_cast<const floatx4*>(as_hj + m);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc = fmaf(a4[q], ym[m + q], acc);
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int w = 0; w < W; ++w) acc[w] = fmaf(a4[q], ym[m + q][w], acc[w]);
   }
-  return acc;
 }
 
-// Q~/K~ (token-major Y, lanes along c): grid (ceil(M*d / 256), 2); stores coalesced along c.
-template <int HMAX>
+template <int W>
+__device__ __forceinline__ void store_halves(half_t* p, const float (&v)[W], float scale) {
+  typedef _Float16 halfw __attribute__((ext_vector_type(W)));
+  halfw h;
+#pragma unroll
+  for (int w = 0; w < W; ++w) h[w] = static_cast<half_t>(v[w] * scale);
+  *reinterpret_cast<halfw*>(p) = h;
+}
+template <>
+__device__ __forceinline__ void store_halves<1>(half_t* p, const float (&v)[1], float scale) {
+  *p = static_cast<half_t>(v[0] * scale);
+}
+
+// Q~/K~ (token-major Y, lanes along c): each thread owns CW consecutive channels of one
+// token (vector loads of Y, CW-wide fp16 stores).  grid (ceil(M*d/CW / 256), 2).
+template <int HMAX, int CW>
 __global__ __launch_bounds__(256) void mix_qk_kernel(ProjArgs pa) {
   extern __shared__ float as[];
   const int which = blockIdx.y;
   const int D = pa.D, d = pa.d, H = pa.H, P = pa.P, N = pa.N;
   stage_alpha<HMAX>(pa.alpha[which], H, P, as);
+  const int groups = d / CW;
   const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (e >= static_cast<int64_t>(pa.B) * N * d) return;
-  const int tok = static_cast<int>(e / d), c = static_cast<int>(e % d);
+  if (e >= static_cast<int64_t>(pa.B) * N * groups) return;
+  const int tok = static_cast<int>(e / groups), c = static_cast<int>(e % groups) * CW;
   const float* __restrict__ y = pa.Yqk + static_cast<int64_t>(tok) * 2 * D + which * D + c;
   half_t* __restrict__ out = (which == 0 ? pa.Q : pa.K) + static_cast<int64_t>(tok) * P * D + c;
   float* __restrict__ oute = which == 0 ? pa.Qe : pa.Ke;
+  const float oscale = which == 0 ? pa.qscale : 1.f;  // Q leaves pre-scaled, in one rounding
   const int b = tok / N, t = tok % N;
-  float ym[HMAX];
+  float ym[HMAX][CW];
 #pragma unroll
-  for (int m = 0; m < HMAX; ++m) ym[m] = y[(m < H ? m : 0) * d];
+  for (int m = 0; m < HMAX; ++m) {
+    const float* src = y + (m < H ? m : 0) * d;
+    if (CW == 4) {
+      const floatx4 v = *reinterpret_cast<const floatx4*>(src);
+#pragma unroll
+      for (int w = 0; w < CW; ++w) ym[m][w] = v[w];
+    } else {
+#pragma unroll
+      for (int w = 0; w < CW; ++w) ym[m][w] = src[w];
+    }
+  }
   for (int h = 0; h < H; ++h)
     for (int j = 0; j < P; ++j) {
-      const float acc = mix_one<HMAX>(as + (h * P + j) * HMAX, ym);
-      out[static_cast<int64_t>(j) * D + h * d] = static_cast<half_t>(acc);
+      float acc[CW];
+      mix_w<HMAX, CW>(as + (h * P + j) * HMAX, ym, acc);
+      store_halves<CW>(out + static_cast<int64_t>(j) * D + h * d, acc, oscale);
       const int i = t * P + j;
-      if (oute && i < pa.R) oute[(static_cast<int64_t>(b) * pa.R + i) * D + h * d + c] = acc;
+      if (oute && i < pa.R) {
+#pragma unroll
+        for (int w = 0; w < CW; ++w) oute[(static_cast<int64_t>(b) * pa.R + i) * D + h * d + c + w] = acc[w];
+      }
     }
 }
 
-// V~^T (channel-major Y, lanes along tokens): grid (ceil(M / 256), d); stores coalesced
-// along t*P + j.
-template <int HMAX>
+// V~^T (channel-major Y, lanes along tokens): each thread owns TW consecutive tokens of one
+// channel row.  When the TW tokens share a sequence and P is even, the TW*P outputs of a head
+// are contiguous and go out as 4-byte pairs.  grid (ceil(M/TW / 256), d).
+template <int HMAX, int TW>
 __global__ __launch_bounds__(256) void mix_v_kernel(ProjArgs pa) {
   extern __shared__ float as[];
   const int c = blockIdx.y;
   const int M = pa.B * pa.N, d = pa.d, H = pa.H, P = pa.P, N = pa.N;
   stage_alpha<HMAX>(pa.alpha[2], H, P, as);
-  const int tok = blockIdx.x * 256 + threadIdx.x;
-  if (tok >= M) return;
-  const int b = tok / N, t = tok % N;
+  const int tok0 = (blockIdx.x * 256 + threadIdx.x) * TW;
+  if (tok0 >= M) return;
   const int64_t L = static_cast<int64_t>(P) * N;
-  float ym[HMAX];
+  float ym[HMAX][TW];
 #pragma unroll
-  for (int m = 0; m < HMAX; ++m) ym[m] = pa.Yvt[static_cast<int64_t>((m < H ? m : 0) * d + c) * M + tok];
+  for (int m = 0; m < HMAX; ++m)
+#pragma unroll
+    for (int w = 0; w < TW; ++w)
+      ym[m][w] = tok0 + w < M ? pa.Yvt[static_cast<int64_t>((m < H ? m : 0) * d + c) * M + tok0 + w] : 0.f;
+  const int b0 = tok0 / N, t0 = tok0 % N;
+  const bool paired = (P % 2 == 0) && (t0 + TW <= N) && (tok0 + TW <= M);
+  typedef _Float16 half2v __attribute__((ext_vector_type(2)));
   for (int h = 0; h < H; ++h) {
-    half_t* __restrict__ vrow = pa.Vt + (static_cast<int64_t>(b * H + h) * d + c) * L + static_cast<int64_t>(t) * P;
-    float* __restrict__ erow = pa.Vte ? pa.Vte + (static_cast<int64_t>(b * H + h) * d + c) * pa.R : nullptr;
+    if (paired) {
+      // Outputs (t, j) and (t, j + 1) are adjacent: 4-byte stores.
+      half_t* __restrict__ vrow = pa.Vt + (static_cast<int64_t>(b0 * H + h) * d + c) * L;
+      for (int j = 0; j < P; j += 2) {
+        float a0[TW], a1[TW];
+        mix_w<HMAX, TW>(as + (h * P + j) * HMAX, ym, a0);
+        mix_w<HMAX, TW>(as + (h * P + j + 1) * HMAX, ym, a1);
+#pragma unroll
+        for (int w = 0; w < TW; ++w) {
+          const int i = (t0 + w) * P + j;
+          const half2v v = {static_cast<half_t>(a0[w]), static_cast<half_t>(a1[w])};
+          *reinterpret_cast<half2v*>(vrow + i) = v;
+          if (pa.Vte && i < pa.R) {
+            float* erow = pa.Vte + (static_cast<int64_t>(b0 * H + h) * d + c) * pa.R;
+            erow[i] = a0[w];
+            if (i + 1 < pa.R) erow[i + 1] = a1[w];
+          }
+        }
+      }
+      continue;
+    }
     for (int j = 0; j < P; ++j) {
-      const float acc = mix_one<HMAX>(as + (h * P + j) * HMAX, ym);
-      vrow[j] = static_cast<half_t>(acc);
-      const int i = t * P + j;
-      if (erow && i < pa.R) erow[i] = acc;
+      float acc[TW];
+      mix_w<HMAX, TW>(as + (h * P + j) * HMAX, ym, acc);
+#pragma unroll
+      for (int w = 0; w < TW; ++w) {
+        const int tok = tok0 + w;
+        if (tok >= M) break;
+        const int b = tok / N, t = tok % N;
+        half_t* __restrict__ vrow = pa.Vt + (static_cast<int64_t>(b * H + h) * d + c) * L;
+        vrow[static_cast<int64_t>(t) * P + j] = static_cast<half_t>(acc[w]);
+        const int i = t * P + j;
+        if (pa.Vte && i < pa.R) pa.Vte[(static_cast<int64_t>(b * H + h) * d + c) * pa.R + i] = acc[w];
+      }
     }
   }
 }
 
 template <int HMAX>
 void launch_mix(const ProjArgs& pa, hipStream_t s) {
+  constexpr int CW = HMAX <= 20 ? 4 : HMAX <= 32 ? 2 : 1;
+  constexpr int TW = HMAX <= 32 ? 2 : 1;
   const int64_t M = static_cast<int64_t>(pa.B) * pa.N;
   const size_t lds = static_cast<size_t>(pa.H) * pa.P * HMAX * sizeof(float);
-  hipLaunchKernelGGL((mix_qk_kernel<HMAX>), dim3(static_cast<unsigned>((M * pa.d + 255) / 256), 2), dim3(256), lds, s, pa);
-  hipLaunchKernelGGL((mix_v_kernel<HMAX>), dim3(static_cast<unsigned>((M + 255) / 256), pa.d), dim3(256), lds, s, pa);
+  const int64_t nqk = M * (pa.d / CW);
+  hipLaunchKernelGGL((mix_qk_kernel<HMAX, CW>), dim3(static_cast<unsigned>((nqk + 255) / 256), 2), dim3(256), lds, s, pa);
+  const int64_t nv = (M + TW - 1) / TW;
+  hipLaunchKernelGGL((mix_v_kernel<HMAX, TW>), dim3(static_cast<unsigned>((nv + 255) / 256), pa.d), dim3(256), lds, s, pa);
 }
 
 }  // namespace
@@ -238,8 +339,7 @@ hipError_t launch_proj_bf16(const ProjArgs& pa, hipStream_t s, hipEvent_t ev_pre
   g1.J = 2 * D;
   g1.K = D;
   g1.ldc = 2 * D;
-  const int t1 = ((g1.I + GT - 1) / GT) * ((g1.J + GT - 1) / GT);
-  hipLaunchKernelGGL(gemm_nt_bf16_kernel, dim3(t1), dim3(256), 0, s, g1);
+  if ((e = launch_gemm_nt(g1, s)) != hipSuccess) return e;
   NtArgs g2{};  // Y_V^T = Wt_V * X^T
   g2.A = pa.Wt + static_cast<int64_t>(2) * D * D;
   g2.B = pa.X;
@@ -248,10 +348,7 @@ hipError_t launch_proj_bf16(const ProjArgs& pa, hipStream_t s, hipEvent_t ev_pre
   g2.J = M;
   g2.K = D;
   g2.ldc = M;
-  const int t2 = ((g2.I + GT - 1) / GT) * ((g2.J + GT - 1) / GT);
-  hipLaunchKernelGGL(gemm_nt_bf16_kernel, dim3(t2), dim3(256), 0, s, g2);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if ((e = launch_gemm_nt(g2, s)) != hipSuccess) return e;
   if (pa.H <= 4) launch_mix<4>(pa, s);
   else if (pa.H <= 8) launch_mix<8>(pa, s);
   else if (pa.H <= 16) launch_mix<16>(pa, s);
