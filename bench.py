@@ -1,19 +1,20 @@
 #!/usr/bin/env python3
 """Throughput of the IHA forward pass on one MI355X.
 
-A step is one whole forward (weight transpose, projection GEMMs + mixing, attention,
+A step is one whole forward (weight transpose, projection GEMMs, mixing, attention,
 first-rows recomputation, collapse) over one batch of synthetic inputs that are resident in
 HBM before timing.
-Prints one JSON line: pseudo-tokens/s for the whole forward, per-kernel times from HIP
-events recorded on the launch stream around every kernel of every timed step, the
-roofline position of the dominant kernel and of attention, and the CPU oracle timed on
-a bounded sample of the same workload.
+Prints one JSON line: pseudo-tokens/s for the whole forward, per-step times from HIP events
+recorded on the launch stream between the kernels of every timed step, the roofline
+position of the dominant step and of every step, the same figures (fewer steps) for the
+other headline workloads, and the CPU oracle timed on a bounded sample of the main workload.
 
 Work per unit (algorithmic, the count the pages' convention gives):
   attention  4 * d flops per visible (query, key) pair: QK^T and AV at 2 flops per
              multiply-add (textbook eq. 5.34), masked pairs and softmax not counted
-  projection 6 * D^2 flops per token (three D x D projections, eq. 5.34) plus the
-             mixing, 6 * D * H * P flops per token (Algorithm 1)
+  gemm       6 * D^2 flops per token (the three D x D projections, eq. 5.34)
+  mix        bytes: 3 * D * 4 read (projected values, fp32) + 3 * P * D * 2 written
+             (stacked fp16 Q~, K~, V~) per token
   collapse   bytes: P*H*d*4 read + H*d*4 written per token
   prep       bytes: 3*D^2*2 read + 3*D^2*2 written (bf16 weight transpose)
 """
@@ -41,28 +42,26 @@ def allowed_pairs(L, mask, window):
     return W * (W + 1) // 2 + (L - W) * W
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="iha_window_p2_b4_n4096")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=64,
-                    help="tokens the CPU oracle computes for the baseline sample")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the forward shards by sequence across GPUs with no exchange; see the design notes)",
-              file=sys.stderr)
-        sys.exit(2)
+STEPS = ["prep", "gemm", "mix", "attention", "first_rows", "collapse"]
 
+
+def roof(kind, work, ms):
+    if kind == "mfma":
+        a = work / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(a, 2), "peak": PEAK_MFMA_F16 / 1e12,
+                "unit": "TFLOP/s", "frac": round(a / (PEAK_MFMA_F16 / 1e12), 4), "traffic": None}
+    a = work / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+            "frac": round(a / (PEAK_HBM / 1e9), 4), "traffic": None}
+
+
+def run_workload(w, steps, warmup):
+    """Time `steps` forwards of workload `w` (after `warmup`); returns inputs and figures."""
     import numpy as np
     import torch
     import interleaved_head_layer_amd as iha
     from interleaved_head_layer_amd import workloads as wl
 
-    w = wl.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     x = wl.make_inputs(w)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -78,49 +77,77 @@ def main():
         iha.iha_forward(X, WQ, WK, WV, aQ, aK, aV, R, w.H, w.P, w.mask, w.window,
                         out=out, workspace=ws, events=events)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(iha.TIMED_EVENTS)]
+           for _ in range(steps)]
     for e in evs:               # create the events before the timed region
         for ev in e:
             ev.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     assert bool(torch.isfinite(out).all()), "non-finite output"
+    del X, WQ, WK, WV, aQ, aK, aV, R, ws, out
+    torch.cuda.empty_cache()
 
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    names = ["prep", "proj_mix", "attention", "first_rows", "collapse"]
-    kms = {n: float(np.mean([evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)]))
-           for k, n in enumerate(names)}
-
+    ms_step = (t1 - t0) * 1e3 / steps
+    kms = {n: float(np.mean([evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(steps)]))
+           for k, n in enumerate(STEPS)}
     B, N, D, H, P, d = w.B, w.N, w.D, w.H, w.P, w.d
     L = P * N
-    pairs = allowed_pairs(L, w.mask, w.window)
-    attn_flops = 4.0 * d * B * H * pairs
-    proj_flops = 6.0 * B * N * D * D + 6.0 * B * N * D * H * P
-    collapse_bytes = B * N * (P * H * d * 4 + H * d * 4) + H * H * P * 4
-    prep_bytes = 3 * D * D * 2 * 2
-
-    def roof(kind, work, ms):
-        if kind == "mfma":
-            a = work / (ms * 1e-3) / 1e12
-            return {"bound": "mfma", "achieved": round(a, 2), "peak": PEAK_MFMA_F16 / 1e12,
-                    "unit": "TFLOP/s", "frac": round(a / (PEAK_MFMA_F16 / 1e12), 4), "traffic": None}
-        a = work / (ms * 1e-3) / 1e9
-        return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                "frac": round(a / (PEAK_HBM / 1e9), 4), "traffic": None}
-
-    roofs = {"prep": roof("hbm", prep_bytes, kms["prep"]),
-             "proj_mix": roof("mfma", proj_flops, kms["proj_mix"]),
+    attn_flops = 4.0 * d * B * H * allowed_pairs(L, w.mask, w.window)
+    roofs = {"prep": roof("hbm", 3 * D * D * 2 * 2, kms["prep"]),
+             "gemm": roof("mfma", 6.0 * B * N * D * D, kms["gemm"]),
+             "mix": roof("hbm", B * N * (3 * D * 4 + 3 * P * D * 2), kms["mix"]),
              "attention": roof("mfma", attn_flops, kms["attention"]),
-             "collapse": roof("hbm", collapse_bytes, kms["collapse"])}
-    dominant = max(kms, key=kms.get)
-    value = B * P * N / (ms_step * 1e-3)
+             "collapse": roof("hbm", B * N * (P * H * d * 4 + H * d * 4) + H * H * P * 4,
+                              kms["collapse"])}
+    return x, {"ms_step": ms_step, "value": B * P * N / (ms_step * 1e-3), "kms": kms,
+               "roofs": roofs}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="iha_window_p2_b4_n4096")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=64,
+                    help="tokens the CPU oracle computes for the baseline sample")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other headline workloads")
+    ap.add_argument("--extra-steps", type=int, default=5)
+    ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB (reference for HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the forward shards by sequence across GPUs with no exchange)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    from interleaved_head_layer_amd import workloads as wl
+
+    if args.copy_ref > 0:
+        import torch
+        src = torch.ones(args.copy_ref << 18, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    w = wl.WORKLOADS[args.workload]
+    x, r = run_workload(w, args.steps, args.warmup)
+    kms, roofs = r["kms"], r["roofs"]
+    dominant = max(roofs, key=lambda k: kms[k])
+    B, N, D, H, P, d = w.B, w.N, w.D, w.H, w.P, w.d
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -135,11 +162,25 @@ def main():
                "sample": f"{len(tok)} uniformly drawn tokens of {w.name} (all their heads and "
                          f"pseudo-tokens, plus the key/value projections they can see), "
                          f"{cs:.1f} s wall in IEEE double"}
+    del x
+
+    extra = {}
+    if not args.no_extra:
+        for name in wl.HEADLINE:
+            if name == w.name:
+                continue
+            _, e = run_workload(wl.WORKLOADS[name], args.extra_steps, 2)
+            extra[name] = {"ms_per_step": round(e["ms_step"], 4),
+                           "pseudo_tokens_per_s": round(e["value"], 1),
+                           "attention": dict(e["roofs"]["attention"],
+                                             ms=round(e["kms"]["attention"], 4)),
+                           "gemm": e["roofs"]["gemm"],
+                           "kernels_ms": {k: round(v, 4) for k, v in e["kms"].items()}}
 
     line = {
         "metric": "IHA fwd pseudo-tokens/s + attention TFLOP/s (% of MI355X bf16 MFMA peak)",
-        "value": round(value, 1), "unit": "pseudo-tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "value": round(r["value"], 1), "unit": "pseudo-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_step"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp16-mfma/fp32-acc" if w.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": w.name, "B": B, "N": N, "D": D, "H": H, "d": d, "P": P,
@@ -150,6 +191,7 @@ def main():
                           tflops=roofs["attention"]["achieved"]),
         "kernels_ms": {k: round(v, 4) for k, v in kms.items()},
         "kernel_roofline": roofs,
+        "other_workloads": extra,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -118,12 +118,15 @@ iha_status iha_forward(const iha_problem* prob, const void* X, const void* W_Q, 
                        const float* alpha_V, const float* R, float* X_out, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 
-/* iha_forward that also records events[0..5] on `stream` around its steps:
- * [0] start, [1] after the weight preparation (bf16: transpose; fp32: mixing
- * folded into the weights), [2] after the projections and the mixing, [3]
- * after the attention kernel, [4] after the fp32 recomputation of the first
- * stacked rows (no work for IHA_F32 or IHA_MASK_NONE), [5] after the collapse.
- * The events are created by the caller (hipEventCreate) and must not be NULL. */
+/* iha_forward that also records IHA_TIMED_EVENTS events on `stream` around its
+ * steps: [0] start, [1] after the weight preparation (bf16: transpose; fp32:
+ * mixing folded into the weights), [2] after the projection GEMMs, [3] after the
+ * mixing (fp32: no separate mixing, recorded right after [2]), [4] after the
+ * attention kernel, [5] after the fp32 recomputation of the first stacked rows
+ * (no work for IHA_F32 or IHA_MASK_NONE), [6] after the collapse.
+ * The events are created by the caller (hipEventCreate) and must not be NULL;
+ * a NULL array or entry returns IHA_ERR_INVALID_ARG before any launch. */
+#define IHA_TIMED_EVENTS 7
 iha_status iha_forward_timed(const iha_problem* prob, const void* X, const void* W_Q,
                              const void* W_K, const void* W_V, const float* alpha_Q,
                              const float* alpha_K, const float* alpha_V, const float* R,

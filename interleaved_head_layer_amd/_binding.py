@@ -18,6 +18,7 @@ STATUS_NAMES = ["IHA_OK", "IHA_ERR_INVALID_ARG", "IHA_ERR_SHAPE", "IHA_ERR_EMPTY
 IHA_MASK_NONE, IHA_MASK_CAUSAL, IHA_MASK_WINDOW = 0, 1, 2
 IHA_F32, IHA_BF16 = 0, 1
 IHA_FLAG_CHECK = 1
+TIMED_EVENTS = 7       # IHA_TIMED_EVENTS in include/iha.h
 _MASKS = {"none": IHA_MASK_NONE, "causal": IHA_MASK_CAUSAL, "window": IHA_MASK_WINDOW}
 
 
@@ -109,9 +110,10 @@ def iha_forward(X, W_Q, W_K, W_V, alpha_Q, alpha_K, alpha_V, R, H: int, P: int, 
     """IHA forward (Algorithm 1).  X [B, N, D] bf16 or fp32 on the GPU; W_* [D, D] same dtype;
     alpha_* [H, H, P] and R [H, H*P] fp32.  Returns X~ [B, N, D] fp32.
 
-    ``events``: optional list of 6 torch.cuda.Event(enable_timing=True), recorded around the
-    steps (start, mixing, GEMM, attention, first-rows recomputation, collapse) on the current
-    stream."""
+    ``events``: optional list of TIMED_EVENTS (7) torch.cuda.Event(enable_timing=True),
+    recorded on the current stream at: start, after the weight preparation, after the
+    projection GEMMs, after the mixing, after attention, after the first-rows
+    recomputation, after the collapse."""
     import torch
     if X.dim() != 3:
         raise ValueError("X must be [B, N, D]")
@@ -138,12 +140,12 @@ def iha_forward(X, W_Q, W_K, W_V, alpha_Q, alpha_K, alpha_V, R, H: int, P: int, 
     if events is None:
         st = lib.iha_forward(ctypes.byref(prob), *args, stream)
     else:
-        if len(events) != 6:
-            raise ValueError("events must hold 6 torch.cuda.Event objects")
+        if len(events) != TIMED_EVENTS:
+            raise ValueError(f"events must hold {TIMED_EVENTS} torch.cuda.Event objects")
         for e in events:
             if e.cuda_event == 0:     # create the underlying event
                 e.record()
-        evs = (ctypes.c_void_p * 6)(*[e.cuda_event for e in events])
+        evs = (ctypes.c_void_p * TIMED_EVENTS)(*[e.cuda_event for e in events])
         st = lib.iha_forward_timed(ctypes.byref(prob), *args, stream, evs)
     if st != IHA_OK:
         raise IHAError(st, "iha_forward")

@@ -171,7 +171,7 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
     pa.R = lay.R;
     pa.qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
     IHA_HIP(iha::launch_clear_flag(flag, stream));
-    IHA_HIP(iha::launch_proj_bf16(pa, stream, ev ? ev[1] : nullptr));
+    IHA_HIP(iha::launch_proj_bf16(pa, stream, ev ? ev[1] : nullptr, ev ? ev[2] : nullptr));
   } else {
     // Step 1: mixing folded into the weights (fp32); step 2: fp32 projection GEMM.
     iha::FoldArgs fa{};
@@ -205,8 +205,9 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
     g.H = H;
     g.d = d;
     IHA_HIP(iha::launch_gemm_f32(g, stream));
+    if (ev) IHA_HIP(hipEventRecord(ev[2], stream));  // no separate mixing step
   }
-  if (ev) IHA_HIP(hipEventRecord(ev[2], stream));
+  if (ev) IHA_HIP(hipEventRecord(ev[3], stream));
 
   // Step 3: per-head masked attention over the P*N stacked rows.
   iha::AttnArgs at{};
@@ -231,7 +232,7 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
   } else {
     IHA_HIP(iha::launch_attn_f32(at, stream));
   }
-  if (ev) IHA_HIP(hipEventRecord(ev[3], stream));
+  if (ev) IHA_HIP(hipEventRecord(ev[4], stream));
   if (lay.R > 0) {
     // The first stacked rows again, with fp32 intermediates (their outputs are the largest).
     iha::EarlyArgs ea{};
@@ -246,11 +247,11 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
     IHA_HIP(iha::launch_early_attn(ea, at.O, static_cast<int64_t>(at.L) * H * d, p.mask,
                                    std::min(at.window, lay.R), score_scale, stream));
   }
-  if (ev) IHA_HIP(hipEventRecord(ev[4], stream));
+  if (ev) IHA_HIP(hipEventRecord(ev[5], stream));
 
   // Steps 4-5: unstack, collapse with R, concatenate heads.
   IHA_HIP(iha::launch_collapse(at.O, R, X_out, B * N, H, P, d, stream));
-  if (ev) IHA_HIP(hipEventRecord(ev[5], stream));
+  if (ev) IHA_HIP(hipEventRecord(ev[6], stream));
 
   if (p.flags & IHA_FLAG_CHECK) {
     IHA_HIP(iha::launch_check_finite(X_out, static_cast<int64_t>(B) * N * D, flag, stream));
@@ -285,7 +286,7 @@ iha_status iha_forward_timed(const iha_problem* prob, const void* X, const void*
                              float* X_out, void* workspace, size_t workspace_bytes,
                              hipStream_t stream, hipEvent_t* events) {
   if (!events) return IHA_ERR_INVALID_ARG;
-  for (int i = 0; i < 6; ++i)
+  for (int i = 0; i < IHA_TIMED_EVENTS; ++i)
     if (!events[i]) return IHA_ERR_INVALID_ARG;
   return forward_impl(prob, X, W_Q, W_K, W_V, alpha_Q, alpha_K, alpha_V, R, X_out, workspace,
                       workspace_bytes, stream, events);

@@ -72,7 +72,7 @@ struct ProjArgs {
   float qscale;           // factor applied to the fp16 Q (the base-2 score scale)
 };
 // ev_prep (may be null) is recorded after the weight transpose.
-hipError_t launch_proj_bf16(const ProjArgs& pa, hipStream_t s, hipEvent_t ev_prep);
+hipError_t launch_proj_bf16(const ProjArgs& pa, hipStream_t s, hipEvent_t ev_prep, hipEvent_t ev_gemm);
 
 // fp32 copies of the first R stacked rows (R = min(128, P*N)) of every (b, h) for bf16
 // inputs under a causal or window mask: Qe, Ke [B][R][H][d], Vte [B][H][d][R].

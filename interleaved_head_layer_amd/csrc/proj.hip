@@ -325,7 +325,7 @@ void launch_mix(const ProjArgs& pa, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_proj_bf16(const ProjArgs& pa, hipStream_t s, hipEvent_t ev_prep) {
+hipError_t launch_proj_bf16(const ProjArgs& pa, hipStream_t s, hipEvent_t ev_prep, hipEvent_t ev_gemm) {
   const int D = pa.D, M = pa.B * pa.N;
   hipLaunchKernelGGL(wprep_kernel, dim3(D / 64, D / 64, 3), dim3(256), 0, s, pa);
   hipError_t e = hipGetLastError();
@@ -349,6 +349,7 @@ hipError_t launch_proj_bf16(const ProjArgs& pa, hipStream_t s, hipEvent_t ev_pre
   g2.K = D;
   g2.ldc = M;
   if ((e = launch_gemm_nt(g2, s)) != hipSuccess) return e;
+  if (ev_gemm && (e = hipEventRecord(ev_gemm, s)) != hipSuccess) return e;
   if (pa.H <= 4) launch_mix<4>(pa, s);
   else if (pa.H <= 8) launch_mix<8>(pa, s);
   else if (pa.H <= 16) launch_mix<16>(pa, s);

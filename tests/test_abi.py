@@ -90,7 +90,15 @@ def test_forward_rejects_before_any_launch():
     assert st == bd.STATUS_NAMES.index("IHA_ERR_EMPTY_ROW")
     st = lib.iha_attention(1, 64, 2, 128, 0, 0, -1.0, fake, fake, fake, fake, 0, None, None)
     assert st == bd.STATUS_NAMES.index("IHA_ERR_INVALID_ARG")
-    evs = (ctypes.c_void_p * 6)()
+    evs = (ctypes.c_void_p * bd.TIMED_EVENTS)()
     st = lib.iha_forward_timed(ctypes.byref(p), *args[:8], fake, fake, ctypes.c_size_t(1 << 40),
                                None, evs)
     assert st == bd.STATUS_NAMES.index("IHA_ERR_INVALID_ARG")   # null events
+
+
+def test_timed_event_count_matches_header():
+    """The binding's event count is the one include/iha.h declares."""
+    import re
+    hdr = open(os.path.join(ROOT, "include", "iha.h")).read()
+    m = re.search(r"#define\s+IHA_TIMED_EVENTS\s+(\d+)", hdr)
+    assert m and int(m.group(1)) == bd.TIMED_EVENTS
