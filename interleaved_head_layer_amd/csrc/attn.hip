@@ -5,10 +5,10 @@
 // sliding window (figure 1) on the interleaved stacked position.
 //
 // Flash-style: the PN x PN score matrix is never formed (the textbook's eq. 5.35 shows
-// why); key tiles stream through LDS and each query row keeps a running maximum and
-// sum (the shift invariance of softmax, textbook section 5.2, makes the rescaling exact).
-// Scores are kept in base 2: s2 = (q . k) * log2(e)/sqrt(d), p = exp2(s2 - max).  The factor
-// is applied to Q as it is loaded (a caller that stored Q pre-scaled passes 1, which is exact).
+// why); key tiles stream through LDS and each query row keeps a running offset and sum
+// (the shift invariance of softmax, textbook section 5.2, makes any offset exact).  Scores
+// are kept in base 2: s2 = (q . k) * log2(e)/sqrt(d), p = exp2(s2 - m).  The factor is
+// applied to Q as it is loaded (a caller that stored Q pre-scaled passes 1, which is exact).
 //
 // A valid query always sees itself (window >= 1 is checked on the host), so its sum is
 // at least 1; a row whose sum is zero is reported through the flag word, never divided.
@@ -155,32 +155,54 @@ struct RowState {
   floatx16 o[NCB];  // O^T accumulators
 };
 
-// Softmax rescaling threshold, base 2: the running maximum is only moved (and O, l rescaled)
-// when a new score exceeds it by more than this, so the probabilities fed to the matrix
-// cores stay <= 2^8 (fp16-safe) and the rescale is rare.  Shift invariance of softmax
-// makes any such choice of the subtracted maximum exact.
-constexpr float kRescaleLog2 = 8.f;
+// Probabilities are computed against the row's current offset m (stale maximum) without a
+// per-tile maximum: the lane's tile sum decides.  A sum <= 2^12 bounds every p by 2^12, well
+// inside fp16; a larger (or non-finite) sum, or a row with no offset yet, takes the slow
+// path that moves m to the row maximum.  Shift invariance of softmax (any subtracted constant
+// cancels in the normalisation) makes every such offset exact.  Q is pre-scaled by
+// log2(e)/sqrt(d), so scores are base 2; the score product starts from the accumulator -m,
+// so its output is already s - m and feeds exp2 directly.
+constexpr float kTileSumMax = 4096.f;
 
-// One key tile for one wave.  Q is pre-scaled by log2(e)/sqrt(d), so scores are in base 2;
-// the score product starts from the accumulator -m (the row's running maximum), so its
-// output is already s - m and feeds exp2 directly.
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 template <int DH, int MASK>
 __device__ __forceinline__ void attn_tile(bool edge, const half_t* __restrict__ ks, const half_t* __restrict__ vs,
                                           const half8 (&qf)[DH / 16], RowState<DH / 32>& st, floatx16& negm,
                                           int k0, int qrow, int L, int window, int krow, int l32, int hf) {
   constexpr int KLD = AttnSmem<DH>::KLD, VLD = AttnSmem<DH>::VLD;
   constexpr int NKS = DH / 16, NCB = DH / 32;
+  // K fragments i = kstep * 2 + kb, read kPre ahead of their product; the first kPre V^T
+  // fragments are read after the score product so they arrive during the softmax.
+  constexpr int NK = 2 * NKS, kPre = 4;
+  auto kfrag = [&](int i) {
+    const int kr_ = (i & 1) * 32 + krow;
+    return *reinterpret_cast<const half8*>(&ks[kr_ * KLD + (((i >> 1) * 2 + hf) ^ kswz<DH>(kr_)) * 8]);
+  };
+  auto vfrag = [&](int j) {  // j = (kb * 2 + s2) * NCB + cb
+    const int cb = j % NCB, ks2 = j / NCB;
+    const int vr_ = cb * 32 + l32;
+    return *reinterpret_cast<const half8*>(&vs[vr_ * VLD + (((ks2 >> 1) * 4 + 2 * hf + (ks2 & 1)) ^ vswz(vr_)) * 8]);
+  };
+  half8 kr[NK];
+#pragma unroll
+  for (int i = 0; i < kPre; ++i) kr[i] = kfrag(i);
   floatx16 s[2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-    for (int kstep = 0; kstep < NKS; ++kstep) {
-      const int kr_ = kb * 32 + krow;
-      const half8 kf = *reinterpret_cast<const half8*>(&ks[kr_ * KLD + ((kstep * 2 + hf) ^ kswz<DH>(kr_)) * 8]);
-      s[kb] = mfma32(kf, qf[kstep], kstep == 0 ? negm : s[kb]);
-    }
+  for (int i = 0; i < NK; ++i) {
+    if (i + kPre < NK) kr[i + kPre] = kfrag(i + kPre);
+    s[i & 1] = mfma32(kr[i], qf[i >> 1], i < 2 ? negm : s[i & 1]);
   }
+  constexpr int NV = 4 * NCB;
+  half8 vr[NV];
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) vr[j] = vfrag(j);
+  __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    if (i + kPre < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
   if (__builtin_expect(edge, false)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -188,22 +210,41 @@ __device__ __forceinline__ void attn_tile(bool edge, const half_t* __restrict__ 
       for (int r = 0; r < 16; ++r)
         if (!visible<MASK>(qrow, k0 + kb * 32 + 16 * hf + r, L, window)) s[kb][r] = -__builtin_inff();
   }
-  float mx = s[0][0];
+  half8 pf[2][2];
+  auto probs = [&]() __attribute__((always_inline)) {
+    const half2v ones = {static_cast<half_t>(1.f), static_cast<half_t>(1.f)};
+    float psum = 0.f;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-  {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    mx = fmaxf(fmaxf(mx, __uint_as_float(sw[0])), __uint_as_float(sw[1]));
-  }
-  // mx is relative to the current offset.  A row moves its maximum at its first visible key
-  // or when a score exceeds it by more than 2^8; the others keep alpha = 1, delta = 0.
-  const bool first = st.m == -__builtin_inff();
-  const bool need = first ? (mx > -__builtin_inff()) : (mx > kRescaleLog2);
-  if (__builtin_expect(__any(need), 0)) {
+      for (int r = 0; r < 16; r += 2) {
+        const floatx2 e2 = {fast_exp2(s[kb][r]), fast_exp2(s[kb][r + 1])};
+        const half2v pr = __builtin_convertvector(e2, half2v);
+        pf[kb][r >> 3][r & 7] = pr[0];
+        pf[kb][r >> 3][(r & 7) + 1] = pr[1];
+        psum = __builtin_amdgcn_fdot2(pr, ones, psum, false);
+      }
+    return psum;
+  };
+  // Slow path: a row without an offset yet (its first visible keys), or a tile whose
+  // probabilities relative to the offset grew past 2^12 in sum (some p > 2^7 could approach
+  // the fp16 range), or a non-finite sum.  The offset then moves to the row maximum and O
+  // and l are rescaled; otherwise the tile never computes a maximum at all.
+  float tsum = probs();
+  const bool unset = st.m == -__builtin_inff();
+  if (__builtin_expect(__any(unset || !(tsum <= kTileSumMax)), 0)) {
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(fmaxf(mx, __uint_as_float(sw[0])), __uint_as_float(sw[1]));
+    }
+    const bool need = unset ? (mx > -__builtin_inff()) : (mx > 0.f);
     const float delta = need ? mx : 0.f;
-    const float alpha = !need ? 1.f : first ? 0.f : fast_exp2(-mx);
+    const float alpha = !need ? 1.f : unset ? 0.f : fast_exp2(-mx);
     st.l *= alpha;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
@@ -213,39 +254,24 @@ __device__ __forceinline__ void attn_tile(bool edge, const half_t* __restrict__ 
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] -= delta;
-    if (need) st.m = first ? mx : st.m + mx;
+    if (need) st.m = unset ? mx : st.m + mx;
     const float nm = st.m == -__builtin_inff() ? 0.f : -st.m;
 #pragma unroll
     for (int r = 0; r < 16; ++r) negm[r] = nm;
+    tsum = probs();
   }
-  half8 pf[2][2];
+  st.l += tsum;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int j = 0; j < NV; ++j) {
+    if (j + kPre < NV) vr[j + kPre] = vfrag(j + kPre);
+    const int ks2 = j / NCB;
+    st.o[j % NCB] = mfma32(vr[j], pf[ks2 >> 1][ks2 & 1], st.o[j % NCB]);
+  }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) pf[kb][r >> 3][r & 7] = static_cast<half_t>(fast_exp2(s[kb][r]));
-  // Row sum of the rounded probabilities (the values the V product uses), fp32 accumulate.
-  const half2v ones = {static_cast<half_t>(1.f), static_cast<half_t>(1.f)};
-  float psum = st.l;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const half2v pr = {pf[kb][s2][2 * e], pf[kb][s2][2 * e + 1]};
-        psum = __builtin_amdgcn_fdot2(pr, ones, psum, false);
-      }
-  st.l = psum;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const int vr_ = cb * 32 + l32;
-        const half8 vf = *reinterpret_cast<const half8*>(&vs[vr_ * VLD + ((kb * 4 + 2 * hf + s2) ^ vswz(vr_)) * 8]);
-        st.o[cb] = mfma32(vf, pf[kb][s2], st.o[cb]);
-      }
+  for (int j = 0; j < NV; ++j) {
+    if (j + kPre < NV) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
 }
 
 template <int DH, int MASK, bool DIRECT>
