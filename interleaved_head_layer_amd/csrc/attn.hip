@@ -299,26 +299,33 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
   const half_t* __restrict__ Vb = static_cast<const half_t*>(a.Vt) + static_cast<int64_t>(b * H + h) * DH * L;
   float* __restrict__ Ob = a.O + static_cast<int64_t>(b) * L * rs + h * DH;
 
+  // Q fragments: all loads in flight at once (rows past the end read the last row, whose
+  // results are never stored), then the first K/V tile, then the optional scale.
   const int qrow = q0 + w * 32 + l32;
+  const int qload = min(qrow, L - 1);
   half8 qf[NKS];
 #pragma unroll
-  for (int s = 0; s < NKS; ++s) {
-    if (qrow < L) {
-      qf[s] = *reinterpret_cast<const half8*>(Qb + qrow * rs + s * 16 + 8 * hf);
-      // Base-2 score scale folded into Q (exact when qk_scale == 1).
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[s][e] = static_cast<half_t>(static_cast<float>(qf[s][e]) * a.qk_scale);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[s][e] = static_cast<half_t>(0.f);
-    }
-  }
+  for (int s = 0; s < NKS; ++s) qf[s] = *reinterpret_cast<const half8*>(Qb + static_cast<int64_t>(qload) * rs + s * 16 + 8 * hf);
 
   int klo = 0, khi = L;
   if (MASK != kMaskNone) khi = min(L, q0 + ABM);
   if (MASK == kMaskWindow) klo = max(0, q0 - window + 1);
   const int kt0 = klo / ABN, kt1 = (khi + ABN - 1) / ABN;
 
+  TileCopy<DH, DIRECT> cp;
+  cp.init(Kb, Vb, rs, L, h);
+  if (kt0 < kt1) {
+    cp.issue(Kb, Vb, kt0 * ABN, sm.k[0], sm.v[0]);
+    cp.commit(sm.k[0], sm.v[0]);
+  }
+
+  // Base-2 score scale folded into Q (skipped when the caller stored Q pre-scaled).
+  if (a.qk_scale != 1.f) {
+#pragma unroll
+    for (int s = 0; s < NKS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[s][e] = static_cast<half_t>(static_cast<float>(qf[s][e]) * a.qk_scale);
+  }
   floatx16 negm;
 #pragma unroll
   for (int r = 0; r < 16; ++r) negm[r] = 0.f;
@@ -329,13 +336,6 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
   for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) st.o[cb][r] = 0.f;
-
-  TileCopy<DH, DIRECT> cp;
-  cp.init(Kb, Vb, rs, L, h);
-  if (kt0 < kt1) {
-    cp.issue(Kb, Vb, kt0 * ABN, sm.k[0], sm.v[0]);
-    cp.commit(sm.k[0], sm.v[0]);
-  }
   wait_global_loads();
   __syncthreads();
 
