@@ -42,6 +42,31 @@ def allowed_pairs(L, mask, window):
     return W * (W + 1) // 2 + (L - W) * W
 
 
+def counter_traffic(workload, step):
+    """HBM bytes per step of `step` from the committed rocprofv3 counter summary of
+    `workload` (FETCH_SIZE and WRITE_SIZE per dispatch, scaled by the copy reference), or
+    None if there is none or the kernel's source changed since the counters were taken."""
+    import glob
+    import hashlib
+    import re
+    root = os.path.dirname(os.path.abspath(__file__))
+    for path in glob.glob(os.path.join(root, "profiles", "hbm_counters_*.md")):
+        m = re.search(r"```json\n(.*?)```", open(path).read(), re.S)
+        if not m:
+            continue
+        info = json.loads(m.group(1))
+        if info.get("workload") != workload or step not in info.get("steps", {}):
+            continue
+        st = info["steps"][step]
+        src = os.path.join(root, st["source"])
+        if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != st["sha256"]:
+            return None
+        sc = info["scale"]
+        kib = sum((f * sc["FETCH_SIZE"] + w * sc["WRITE_SIZE"]) * n for f, w, n in st["kernels"].values())
+        return int(kib * 1024)
+    return None
+
+
 STEPS = ["prep", "gemm", "mix", "attention", "first_rows", "collapse"]
 
 
@@ -147,6 +172,8 @@ def main():
     x, r = run_workload(w, args.steps, args.warmup)
     kms, roofs = r["kms"], r["roofs"]
     dominant = max(roofs, key=lambda k: kms[k])
+    for k in roofs:
+        roofs[k]["traffic"] = counter_traffic(w.name, k)
     B, N, D, H, P, d = w.B, w.N, w.D, w.H, w.P, w.d
 
     cpu = None
