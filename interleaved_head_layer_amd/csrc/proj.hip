@@ -311,6 +311,163 @@ __global__ __launch_bounds__(256) void mix_v_kernel(ProjArgs pa) {
   }
 }
 
+// ------------------------------------------------------------------- mixing on the matrix cores
+// The mixing is a small product per channel c: with rows (h, j) of alpha^T and columns
+// tokens,  V~^T_c[(h,j)][t] = sum_m alpha[m][h][j] * Y_V^T[m*d + c][t].  Both operands are
+// split into fp16 high and low parts (x = hi + lo, |lo| <= 2^-11 |x|) and three fp16 products
+// with fp32 accumulation (hi*hi + lo*hi + hi*lo) give the fp32 result to about 2^-21
+// relative, the same as fp32 FMAs; the arithmetic then costs nothing next to the memory
+// traffic.
+__device__ __forceinline__ half_t hi_f16(float x) { return static_cast<half_t>(x); }
+__device__ __forceinline__ half_t lo_f16(float x) {
+  return static_cast<half_t>(x - static_cast<float>(static_cast<half_t>(x)));
+}
+
+// alpha^T operands: A[(h,j) = mb*32 + l%32][k = ks*16 + 8*(l/32) + e] = alpha[m][h][j],
+// zero outside h*P + j < H*P and m < H.
+template <int MB, int KS>
+__device__ __forceinline__ void alpha_operands(const float* __restrict__ al, int H, int P, half8 (&ah)[MB][KS],
+                                               half8 (&alo)[MB][KS]) {
+  const int lane = threadIdx.x & 63, HP = H * P;
+  float a[MB][KS][8];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int row = mb * 32 + (lane & 31), m = ks * 16 + 8 * (lane >> 5) + e;
+        a[mb][ks][e] = al[(row < HP && m < H) ? m * HP + row : 0];
+      }
+  __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the first use
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int row = mb * 32 + (lane & 31), m = ks * 16 + 8 * (lane >> 5) + e;
+        const float v = (row < HP && m < H) ? a[mb][ks][e] : 0.f;
+        ah[mb][ks][e] = hi_f16(v);
+        alo[mb][ks][e] = lo_f16(v);
+      }
+}
+
+// V~^T from Y_V^T.  A wave owns one channel c and 128 tokens of one sequence: lane n (of 32)
+// loads float4s of tokens 4n..4n+3, so column n of product block q is token 4n + q; after the
+// four blocks a lane holds, for each of its (h, j) rows, four consecutive tokens, i.e. 4*P
+// consecutive fp16 of V~^T[b][h][c][*] (P in {1, 2, 4}).  grid (ceil(M / 512), d), 256 threads.
+template <int P, int MB, int KS>
+__global__ __launch_bounds__(256) void mix_v_mfma_kernel(ProjArgs pa) {
+  const int M = pa.B * pa.N, d = pa.d, H = pa.H, N = pa.N;
+  const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
+  // The four waves take consecutive 128-token blocks of one channel: 2 KB runs per row.
+  const int c = blockIdx.y;
+  const int tok0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 128;  // N % 128 == 0: one sequence
+  if (tok0 >= M) return;
+  const int b = tok0 / N, t0 = tok0 % N;
+  // B operands, blocks q = 0..3: B[k][n] = Y_V^T[m = ks*16 + 8*hf + k%8][token 4n + q].
+  half8 bh[4][KS], bl[4][KS];
+  floatx4 yall[KS][8];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int m = ks * 16 + 8 * hf + e;
+      yall[ks][e] = *reinterpret_cast<const floatx4*>(pa.Yvt + static_cast<int64_t>((m < H ? m : 0) * d + c) * M + tok0 + 4 * n);
+    }
+  half8 ah[MB][KS], alo[MB][KS];
+  alpha_operands<MB, KS>(pa.alpha[2], H, P, ah, alo);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    floatx4 y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int m = ks * 16 + 8 * hf + e;
+      y[e] = m < H ? yall[ks][e] : floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bh[q][ks][e] = hi_f16(y[e][q]);
+        bl[q][ks][e] = lo_f16(y[e][q]);
+      }
+  }
+  const int64_t L = static_cast<int64_t>(P) * N;
+  const int HP = H * P;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    floatx16 acc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[q][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        acc[q] = mfma32(ah[mb][ks], bh[q][ks], acc[q]);
+        acc[q] = mfma32(alo[mb][ks], bh[q][ks], acc[q]);
+        acc[q] = mfma32(ah[mb][ks], bl[q][ks], acc[q]);
+      }
+    }
+    // Lane rows: row = mb*32 + 8*(r/4) + 4*hf + r%4 = h*P + j.
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {        // g = r / 4: rows 4*(2g + hf) .. +3
+      const int row0 = mb * 32 + 8 * g + 4 * hf;
+      if (row0 >= HP) continue;
+#pragma unroll
+      for (int u = 0; u < 4 / P; ++u) {  // heads among these 4 rows
+        const int h = (row0 + u * P) / P;
+        if (h >= H) continue;
+        // 4 tokens x P pseudo-tokens of head h, stacked positions (t0 + 4n + q)*P + j
+        typedef _Float16 halfv __attribute__((ext_vector_type(4 * P)));
+        halfv v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int j = 0; j < P; ++j) v[q * P + j] = static_cast<half_t>(acc[q][4 * g + u * P + j]);
+        half_t* dst = pa.Vt + (static_cast<int64_t>(b * H + h) * d + c) * L + static_cast<int64_t>(t0 + 4 * n) * P;
+        *reinterpret_cast<halfv*>(dst) = v;
+        if (pa.Vte && (t0 + 4 * n) * P < pa.R) {
+          float* erow = pa.Vte + (static_cast<int64_t>(b * H + h) * d + c) * pa.R;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+              const int i = (t0 + 4 * n + q) * P + j;
+              if (i < pa.R) erow[i] = acc[q][4 * g + u * P + j];
+            }
+        }
+      }
+    }
+  }
+}
+
+template <int P>
+bool launch_mix_v_mfma_p(const ProjArgs& pa, hipStream_t s) {
+  const int M = pa.B * pa.N;
+  const dim3 grid((M + 511) / 512, pa.d);
+  const int mb = (pa.H * P + 31) / 32, ks = (pa.H + 15) / 16;
+  if (mb == 1 && ks == 1) hipLaunchKernelGGL((mix_v_mfma_kernel<P, 1, 1>), grid, dim3(256), 0, s, pa);
+  else if (mb <= 2 && ks == 1) hipLaunchKernelGGL((mix_v_mfma_kernel<P, 2, 1>), grid, dim3(256), 0, s, pa);
+  else if (mb <= 3 && ks <= 2) hipLaunchKernelGGL((mix_v_mfma_kernel<P, 3, 2>), grid, dim3(256), 0, s, pa);
+  else if (mb <= 4 && ks <= 2) hipLaunchKernelGGL((mix_v_mfma_kernel<P, 4, 2>), grid, dim3(256), 0, s, pa);
+  else return false;
+  return true;
+}
+
+// The matrix-core V mixing: P in {1, 2, 4}, whole 128-token blocks per sequence,
+// H*P <= 128 and H <= 32.  Returns false (nothing launched) otherwise.
+bool launch_mix_v_mfma(const ProjArgs& pa, hipStream_t s) {
+  if (pa.N % 128 != 0 || pa.H > 32 || pa.H * pa.P > 128) return false;
+  switch (pa.P) {
+    case 1: return launch_mix_v_mfma_p<1>(pa, s);
+    case 2: return launch_mix_v_mfma_p<2>(pa, s);
+    case 4: return launch_mix_v_mfma_p<4>(pa, s);
+    default: return false;
+  }
+}
+
 template <int HMAX>
 void launch_mix(const ProjArgs& pa, hipStream_t s) {
   constexpr int CW = HMAX <= 20 ? 4 : HMAX <= 32 ? 2 : 1;
@@ -319,6 +476,7 @@ void launch_mix(const ProjArgs& pa, hipStream_t s) {
   const size_t lds = static_cast<size_t>(pa.H) * pa.P * HMAX * sizeof(float);
   const int64_t nqk = M * (pa.d / CW);
   hipLaunchKernelGGL((mix_qk_kernel<HMAX, CW>), dim3(static_cast<unsigned>((nqk + 255) / 256), 2), dim3(256), lds, s, pa);
+  if (launch_mix_v_mfma(pa, s)) return;
   const int64_t nv = (M + TW - 1) / TW;
   hipLaunchKernelGGL((mix_v_kernel<HMAX, TW>), dim3(static_cast<unsigned>((nv + 255) / 256), pa.d), dim3(256), lds, s, pa);
 }

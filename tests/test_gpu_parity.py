@@ -90,6 +90,12 @@ SMALL = [
     (2, 50, 64, 2, 3, "causal", None, "f32"),        # fp32 path, d = 32
     (1, 70, 256, 2, 2, "window", 9, "f32"),          # fp32 path, d = 128
     (1, 33, 64, 4, 2, "none", None, "f32"),          # fp32 path, d = 16
+    # N a multiple of 128: the V mixing runs on the matrix cores
+    (1, 256, 256, 2, 2, "causal", None, "bf16"),     # H = 2
+    (2, 128, 320, 5, 4, "window", 37, "bf16"),       # H = 5 (odd), P = 4, d = 64
+    (1, 128, 192, 3, 1, "none", None, "bf16"),       # H = 3, P = 1: heads past H skipped
+    (1, 384, 2560, 20, 4, "window", 100, "bf16"),    # H = 20: two k-steps, three row blocks
+    (2, 128, 1024, 16, 2, "causal", None, "bf16"),   # H = 16, P = 2
 ]
 
 
