@@ -78,23 +78,26 @@ struct TileCopy {
   uint4 kr[DIRECT ? 1 : ROUNDS], vr[DIRECT ? 1 : ROUNDS];
   __amdgpu_buffer_rsrc_t krs, vrs;
   unsigned koff[2], voff;
-  int64_t rs;
+  int64_t rs, cs;  // K: halves between keys and between 16-byte d-chunks
   int L;
 
-  __device__ __forceinline__ void init(const half_t* Kb, const half_t* Vb, int64_t rs_, int L_, int h) {
+  // kbytes: bytes of K readable from Kb (reads past them return zero).
+  __device__ __forceinline__ void init(const half_t* Kb, const half_t* Vb, int64_t rs_, int64_t cs_, int L_,
+                                       int64_t kbytes) {
     rs = rs_;
+    cs = cs_;
     L = L_;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     if (DIRECT) {
       krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(Kb), static_cast<short>(0),
-                                              static_cast<int>((L_ * rs_ - static_cast<int64_t>(h) * DH) * 2), 0x00020000);
+                                              static_cast<int>(kbytes), 0x00020000);
       vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(Vb), static_cast<short>(0),
                                               static_cast<int>(static_cast<int64_t>(DH) * L_ * 2), 0x00020000);
       const int rl = (w * 64 + lane) / KCH, pos = (w * 64 + lane) % KCH;
 #pragma unroll
       for (int bit = 0; bit < 2; ++bit) {
         const int sw = (rl & 7) | ((DH == 128 ? bit : 0) << 3);
-        koff[bit] = static_cast<unsigned>((rl * rs_ + (pos ^ sw) * 8) * 2);
+        koff[bit] = static_cast<unsigned>((rl * rs_ + (pos ^ sw) * cs_) * 2);
       }
       const int cl = (w * 64 + lane) / (ABN / 8), vpos = (w * 64 + lane) % (ABN / 8);
       voff = static_cast<unsigned>((static_cast<int64_t>(cl) * L_ + (vpos ^ vswz(cl)) * 8) * 2);
@@ -119,7 +122,7 @@ struct TileCopy {
         const int slot = (p * AWaves + w) * 64 + lane;
         const int r = slot / KCH, pos = slot % KCH;
         const int key = min(k0 + r, L - 1);
-        kr[p] = *reinterpret_cast<const uint4*>(Kb + key * rs + (pos ^ kswz<DH>(r)) * 8);
+        kr[p] = *reinterpret_cast<const uint4*>(Kb + key * rs + (pos ^ kswz<DH>(r)) * cs);
         const int cr = slot / (ABN / 8), vpos = slot % (ABN / 8);
         const int vkey = k0 + (vpos ^ vswz(cr)) * 8;
         const half_t* vsrc = Vb + static_cast<int64_t>(cr) * L + vkey;
@@ -293,9 +296,16 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
-  const int64_t rs = static_cast<int64_t>(H) * DH;  // stride between stacked rows
-  const half_t* __restrict__ Qb = static_cast<const half_t*>(a.Q) + static_cast<int64_t>(b) * L * rs + h * DH;
-  const half_t* __restrict__ Kb = static_cast<const half_t*>(a.K) + static_cast<int64_t>(b) * L * rs + h * DH;
+  const int64_t rs = static_cast<int64_t>(H) * DH;  // stride between stacked rows of O
+  // Q and K: element (row, 16-byte d-chunk cc) of head (b, h) at base + row*qrs + cc*qcs.
+  //   row-major [B][L][H][d]:        base = b*L*H*d + h*d,     qrs = H*d, qcs = 8
+  //   chunked   [B][H][d/8][L][8]:   base = (b*H + h)*d*L,     qrs = 8,   qcs = 8*L
+  const bool chunked = a.qk_layout == kQKChunked;
+  const int64_t qbase = chunked ? static_cast<int64_t>(b * H + h) * DH * L : static_cast<int64_t>(b) * L * rs + h * DH;
+  const int64_t qrs = chunked ? 8 : rs, qcs = chunked ? static_cast<int64_t>(8) * L : 8;
+  const int64_t kbytes = chunked ? static_cast<int64_t>(DH) * L * 2 : (static_cast<int64_t>(L) * rs - h * DH) * 2;
+  const half_t* __restrict__ Qb = static_cast<const half_t*>(a.Q) + qbase;
+  const half_t* __restrict__ Kb = static_cast<const half_t*>(a.K) + qbase;
   const half_t* __restrict__ Vb = static_cast<const half_t*>(a.Vt) + static_cast<int64_t>(b * H + h) * DH * L;
   float* __restrict__ Ob = a.O + static_cast<int64_t>(b) * L * rs + h * DH;
 
@@ -305,7 +315,7 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
   const int qload = min(qrow, L - 1);
   half8 qf[NKS];
 #pragma unroll
-  for (int s = 0; s < NKS; ++s) qf[s] = *reinterpret_cast<const half8*>(Qb + static_cast<int64_t>(qload) * rs + s * 16 + 8 * hf);
+  for (int s = 0; s < NKS; ++s) qf[s] = *reinterpret_cast<const half8*>(Qb + static_cast<int64_t>(qload) * qrs + (2 * s + hf) * qcs);
 
   int klo = 0, khi = L;
   if (MASK != kMaskNone) khi = min(L, q0 + ABM);
@@ -313,7 +323,7 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
   const int kt0 = klo / ABN, kt1 = (khi + ABN - 1) / ABN;
 
   TileCopy<DH, DIRECT> cp;
-  cp.init(Kb, Vb, rs, L, h);
+  cp.init(Kb, Vb, qrs, qcs, L, kbytes);
   if (kt0 < kt1) {
     cp.issue(Kb, Vb, kt0 * ABN, sm.k[0], sm.v[0]);
     cp.commit(sm.k[0], sm.v[0]);

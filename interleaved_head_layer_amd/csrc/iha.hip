@@ -21,7 +21,7 @@ constexpr int64_t kMaxElems = int64_t(1) << 40;  // elements of any one tensor
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t flag, wt, yqk, yvt, q, k, vt, pbar, qe, ke, vte, total;
+  size_t flag, wt, yqk, yvt, ye, q, k, vt, pbar, qe, ke, vte, total;
   int R;  // precise first stacked rows (0 when unused)
 };
 
@@ -69,8 +69,10 @@ Layout layout_of(const iha_problem& p) {
   if (p.dtype == IHA_BF16) {
     // transposed weights, fp32 projections (token-major Q|K, channel-major V)
     L.wt = take(3 * static_cast<size_t>(p.D) * p.D * 2);
-    L.yqk = take(M * 2 * p.D * 4);
-    L.yvt = take(M * p.D * 4);
+    if (!iha::fused_shape(p.H, p.D, p.P)) {
+      L.yqk = take(M * 2 * p.D * 4);
+      L.yvt = take(M * p.D * 4);
+    }
   } else {
     L.wt = take(3 * static_cast<size_t>(p.P) * p.D * p.D * 4);  // folded weights
   }
@@ -85,6 +87,8 @@ Layout layout_of(const iha_problem& p) {
     L.qe = take(static_cast<size_t>(p.B) * R * p.D * 4);
     L.ke = take(static_cast<size_t>(p.B) * R * p.D * 4);
     L.vte = take(static_cast<size_t>(p.B) * R * p.D * 4);
+    if (iha::fused_shape(p.H, p.D, p.P))  // unmixed projections of the first tokens
+      L.ye = take(static_cast<size_t>(p.B) * ((R + p.P - 1) / p.P) * 3 * p.D * 4);
   }
   L.total = off;
   return L;
@@ -140,6 +144,7 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
                  B, N, D, H, d, P, p.mask, static_cast<long long>(p.window), bf16 ? "bf16" : "f32");
 
   if (ev) IHA_HIP(hipEventRecord(ev[0], stream));
+  int qk_layout = iha::kQKRowMajor;
   if (bf16) {
     // Steps 1-2: exact bf16 projections (fp32 accumulation), fp32 mixing into the stacked
     // fp16 layouts (and fp32 copies of the first rows).
@@ -152,8 +157,9 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
     pa.alpha[1] = alpha_K;
     pa.alpha[2] = alpha_V;
     pa.Wt = reinterpret_cast<uint16_t*>(ws + lay.wt);
-    pa.Yqk = reinterpret_cast<float*>(ws + lay.yqk);
-    pa.Yvt = reinterpret_cast<float*>(ws + lay.yvt);
+    const bool fused = iha::fused_shape(H, D, P);  // no fp32 projections in HBM
+    pa.Yqk = fused ? nullptr : reinterpret_cast<float*>(ws + lay.yqk);
+    pa.Yvt = fused ? nullptr : reinterpret_cast<float*>(ws + lay.yvt);
     pa.Q = reinterpret_cast<iha::half_t*>(ws + lay.q);
     pa.K = reinterpret_cast<iha::half_t*>(ws + lay.k);
     pa.Vt = reinterpret_cast<iha::half_t*>(ws + lay.vt);
@@ -161,6 +167,7 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
       pa.Qe = reinterpret_cast<float*>(ws + lay.qe);
       pa.Ke = reinterpret_cast<float*>(ws + lay.ke);
       pa.Vte = reinterpret_cast<float*>(ws + lay.vte);
+      pa.Ye = reinterpret_cast<float*>(ws + lay.ye);
     }
     pa.B = B;
     pa.N = N;
@@ -169,8 +176,10 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
     pa.d = d;
     pa.P = P;
     pa.R = lay.R;
+    pa.T0 = (lay.R + P - 1) / P;
     pa.qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
     IHA_HIP(iha::launch_clear_flag(flag, stream));
+    if (iha::proj_fused(pa)) qk_layout = iha::kQKChunked;
     IHA_HIP(iha::launch_proj_bf16(pa, stream, ev ? ev[1] : nullptr, ev ? ev[2] : nullptr));
   } else {
     // Step 1: mixing folded into the weights (fp32); step 2: fp32 projection GEMM.
@@ -228,6 +237,7 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
   at.qk_scale = score_scale;
   if (bf16) {
     at.qk_scale = 1.f;  // the fp16 Q was stored pre-scaled
+    at.qk_layout = qk_layout;
     IHA_HIP(iha::launch_attn_f16(at, stream));
   } else {
     IHA_HIP(iha::launch_attn_f32(at, stream));

@@ -32,17 +32,22 @@ struct GemmArgs {
 };
 hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s);
 
+// Layouts of Q and K for the fp16 attention kernel.
+constexpr int kQKRowMajor = 0;  // [B][L][H][d]
+constexpr int kQKChunked = 1;   // [B][H][d/8][L][8]: 16-byte d-chunks, contiguous over rows
+
 // Masked attention over the stacked sequence: O = softmax_2(s) V with base-2 scores
 // s = (q . k) * qk_scale.
 struct AttnArgs {
-  const void* Q;   // [B][L][H][d]
-  const void* K;   // [B][L][H][d]
+  const void* Q;   // [B][L][H][d] or chunked (qk_layout; fp16 kernel only)
+  const void* K;   // same layout as Q
   const void* Vt;  // [B][H][d][L]
   float* O;        // [B][L][H][d]
   unsigned* flag;  // may be null
   int B, L, H, d, mask, window;
   float qk_scale;     // multiplies q . k to give base-2 scores
   int64_t o_bstride;  // elements between batches of O (0: L*H*d)
+  int qk_layout;      // kQKRowMajor or kQKChunked
 };
 hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
@@ -68,10 +73,19 @@ struct ProjArgs {
   float* Qe;              // fp32 copies of the first R stacked rows (or null)
   float* Ke;
   float* Vte;
+  float* Ye;              // fused path: [B][T0][3D] unmixed fp32 projections of the first tokens
   int B, N, D, H, d, P, R;
+  int T0;                 // ceil(R / P): tokens whose pseudo-tokens include a first row
   float qscale;           // factor applied to the fp16 Q (the base-2 score scale)
 };
-// ev_prep (may be null) is recorded after the weight transpose.
+inline bool fused_shape(int64_t H, int64_t D, int64_t P) {
+  return H == 16 && D % 256 == 0 && (P == 1 || P == 2 || P == 4);
+}
+// True when the projection runs fused with the mixing (H = 16, D % 256 == 0, P in {1,2,4});
+// Q~ and K~ are then written in the chunked layout [B][H][d/8][P*N][8], else row-major.
+bool proj_fused(const ProjArgs& pa);
+// ev_prep (may be null) is recorded after the weight transpose, ev_gemm after the projection
+// GEMMs (with the fused path: after the fused kernel, the mixing included).
 hipError_t launch_proj_bf16(const ProjArgs& pa, hipStream_t s, hipEvent_t ev_prep, hipEvent_t ev_gemm);
 
 // fp32 copies of the first R stacked rows (R = min(128, P*N)) of every (b, h) for bf16

@@ -20,18 +20,24 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // ------------------------------------------------------------------- W transpose
-// grid: (D/64, D/64, 3); block 256.  64x64 tiles through LDS.
-__global__ __launch_bounds__(256) void wprep_kernel(ProjArgs pa) {
+// grid: (D/64, D/64, 3); block 256.  64x64 tiles through LDS.  With `cm`, column n = m*d + c
+// of W (head m, channel c) goes to row c*H + m instead of row n (the fused mixing wants the H
+// source heads of a channel in consecutive rows).
+__global__ __launch_bounds__(256) void wprep_kernel(ProjArgs pa, int cm) {
   __shared__ uint16_t t[64][65];
   const int which = blockIdx.z;
   const uint16_t* __restrict__ W = pa.W[which];
-  const int D = pa.D;
+  const int D = pa.D, d = pa.d, H = pa.H;
   const int k0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
   const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;
   for (int r = ty; r < 64; r += 4) t[r][tx] = W[static_cast<int64_t>(k0 + r) * D + n0 + tx];
   __syncthreads();
   uint16_t* __restrict__ Wt = pa.Wt + static_cast<int64_t>(which) * D * D;
-  for (int r = ty; r < 64; r += 4) Wt[static_cast<int64_t>(n0 + r) * D + k0 + tx] = t[tx][r];
+  for (int r = ty; r < 64; r += 4) {
+    const int n = n0 + r;
+    const int row = cm ? (n % d) * H + n / d : n;
+    Wt[static_cast<int64_t>(row) * D + k0 + tx] = t[tx][r];
+  }
 }
 
 // ------------------------------------------------------------------- NT GEMM
@@ -52,8 +58,9 @@ struct NtSmem {
   uint16_t b[2][GTJ * GK];
 };
 
-__global__ __launch_bounds__(GThreads, 1) void gemm_nt_bf16_kernel(NtArgs g) {
-  __shared__ __attribute__((aligned(16))) NtSmem sm;
+// Main loop of one 256 x 256 tile; hands the accumulators to epi(acc, i0, j0, wm, wn).
+template <typename Epi>
+__device__ __forceinline__ void gemm_tile(const NtArgs& g, NtSmem& sm, Epi&& epi) {
   const int I = g.I, J = g.J, K = g.K;
   const int ntj = (J + GTJ - 1) / GTJ, nti = (I + GTI - 1) / GTI;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -128,19 +135,149 @@ __global__ __launch_bounds__(GThreads, 1) void gemm_nt_bf16_kernel(NtArgs g) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
-  // Lane l holds C[8*(r/4) + 4*hf + r%4][l%32] of each 32x32 block.
+  epi(acc, i0, j0, wm, wn);
+}
+
+__global__ __launch_bounds__(GThreads, 1) void gemm_nt_bf16_kernel(NtArgs g) {
+  __shared__ __attribute__((aligned(16))) NtSmem sm;
+  gemm_tile(g, sm, [&](floatx16 (&acc)[4][2], int i0, int j0, int wm, int wn) {
+    const int lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5;
+    const int I = g.I, J = g.J;
+    // Lane l holds C[8*(r/4) + 4*hf + r%4][l%32] of each 32x32 block.
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = j0 + wn * 64 + j * 32 + l32;
+        if (col >= J) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = i0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (row < I) g.C[static_cast<int64_t>(row) * g.ldc + col] = acc[i][j][r];
+        }
+      }
+  });
+}
+
+// ------------------------------------------------------------------- fused projection + mixing
+// For H = 16 the weight rows are permuted to (which, c, m) (wprep with cm), so each 32-row
+// block of a tile holds the 16 source heads of two channels and a lane's accumulator
+// registers 0..7 (8..15) are 8 of the 16 source heads of the first (second) channel for one
+// token: exactly the B operand of a 32x32x16 product over the source heads, with k-slot
+// 8*hf + e standing for head m = 8*(e/4) + 4*hf + e%4.  The epilogue mixes in place
+//   out[(h, j)][token] = sum_m alpha[m][h][j] * Y[(c, m)][token]
+// with the fp16 hi/lo split (three products, fp32 accumulation, ~2^-21 relative) and writes
+//   V~^T [B][H][d][P*N]           (P consecutive fp16 per lane and head),
+//   Q~, K~ [B][H][d/8][P*N][8]    (a wave's 8 channels form one 16-byte chunk per row),
+// plus the fp32 first rows; the fp32 projections never reach HBM.
+constexpr int kFusedH = 16;
+
+// mix(o): the mixed values of one channel for one 32-token column block: lane row r is
+// (h, jj) with h*P + jj = mb*32 + 8*(r/4) + 4*hf + r%4, column = the lane's token.
+template <int MB>
+__device__ __forceinline__ floatx16 mix_block(const floatx16& y, int cs, const half8& ah, const half8& alo) {
+  half8 bh, bl;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = y[8 * cs + e];
+    bh[e] = static_cast<half_t>(x);
+    bl[e] = static_cast<half_t>(x - static_cast<float>(bh[e]));
+  }
+  floatx16 o;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) o[r] = 0.f;
+  o = mfma32(ah, bh, o);
+  o = mfma32(alo, bh, o);
+  return mfma32(ah, bl, o);
+}
+
+template <int P>
+__global__ __launch_bounds__(GThreads, 1) void gemm_mix_bf16_kernel(NtArgs g, ProjArgs pa) {
+  __shared__ __attribute__((aligned(16))) NtSmem sm;
+  gemm_tile(g, sm, [&](floatx16 (&acc)[4][2], int i0, int j0, int wm, int wn) {
+    constexpr int H = kFusedH, HP = H * P, MB = (HP + 31) / 32;
+    const int lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5;
+    const int D = pa.D, d = pa.d, N = pa.N, M = g.J;
+    const int which = i0 / D;                       // tiles never straddle Q / K / V
+    const int c0 = ((i0 % D) + 128 * wm) / H;       // the wave's 8 channels: c0 .. c0 + 7
+    const float* __restrict__ al = pa.alpha[which];
+    const int64_t L = static_cast<int64_t>(P) * N;
+    half8 ah[MB], alo[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int row = mb * 32 + l32, m = 8 * (e >> 2) + 4 * hf + (e & 3);
+        const float v = al[row < HP ? m * HP + row : 0];
+        const float a = row < HP ? v : 0.f;
+        ah[mb][e] = static_cast<half_t>(a);
+        alo[mb][e] = static_cast<half_t>(a - static_cast<float>(ah[mb][e]));
+      }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int col = j0 + wn * 64 + j * 32 + l32;
-      if (col >= J) continue;
+      const int tok = j0 + 64 * wn + 32 * j + l32;
+      const bool ok = tok < M;
+      const int b = tok / N, t = tok % N;
+      if (__builtin_expect(__any(ok && t < pa.T0), false)) {
+        // Rare column blocks holding a sequence's first T0 tokens: their unmixed fp32
+        // projections go to Ye[b][t][row] (row = which*D + c*H + m); a small kernel mixes them
+        // into the fp32 first rows.
+        if (ok && t < pa.T0) {
+          float* ye = pa.Ye + (static_cast<int64_t>(b) * pa.T0 + t) * 3 * D + i0 + 128 * wm;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = i0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (row < I) g.C[static_cast<int64_t>(row) * g.ldc + col] = acc[i][j][r];
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ye[32 * i + 8 * (r >> 2) + 4 * hf + (r & 3)] = acc[i][j][r];
+        }
+      }
+      if (which < 2) {
+        // Q~ / K~: a lane gathers 4 of its 8 channels of each row (half of a 16-byte chunk)
+        // at a time, to bound the registers held next to the accumulators.
+        half_t* __restrict__ qk = which == 0 ? pa.Q : pa.K;
+        const float oscale = which == 0 ? pa.qscale : 1.f;  // Q leaves pre-scaled, one rounding
+        half_t* dst = qk + (static_cast<int64_t>(b * H) * (d / 8) + c0 / 8) * L * 8 + static_cast<int64_t>(t) * P * 8;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            half4 stg[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int cl = 4 * half + q;
+              const floatx16 o = mix_block<MB>(acc[cl >> 1][j], cl & 1, ah[mb], alo[mb]);
+#pragma unroll
+              for (int r = 0; r < 16; ++r) stg[r][q] = static_cast<half_t>(o[r] * oscale);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = mb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+              if (ok && row < HP)
+                *reinterpret_cast<half4*>(dst + static_cast<int64_t>(row / P) * (d / 8) * L * 8 + (row % P) * 8 + 4 * half) =
+                    stg[r];
+            }
+          }
+      } else {
+        // V~^T: P consecutive fp16 per lane and head.
+        typedef _Float16 halfp __attribute__((ext_vector_type(P)));
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int cl = 0; cl < 8; ++cl) {
+            const floatx16 o = mix_block<MB>(acc[cl >> 1][j], cl & 1, ah[mb], alo[mb]);
+            const int c = c0 + cl;
+            half_t* dst = pa.Vt + (static_cast<int64_t>(b * H) * d + c) * L + static_cast<int64_t>(t) * P;
+#pragma unroll
+            for (int r0 = 0; r0 < 16; r0 += P) {
+              const int row = mb * 32 + 8 * (r0 >> 2) + 4 * hf + (r0 & 3);  // jj = 0 of head row / P
+              halfp v;
+#pragma unroll
+              for (int jj = 0; jj < P; ++jj) v[jj] = static_cast<half_t>(o[r0 + jj]);
+              if (ok && row < HP) *reinterpret_cast<halfp*>(dst + static_cast<int64_t>(row / P) * d * L) = v;
+            }
+          }
       }
     }
+  });
 }
 
 // Launch C = A B^T, splitting A's rows or B's rows into chunks whose bytes fit the 32-bit
@@ -483,12 +620,72 @@ void launch_mix(const ProjArgs& pa, hipStream_t s) {
 
 }  // namespace
 
+// fp32 first rows of the fused path: the mixing of the unmixed fp32 projections Ye of each
+// sequence's first T0 tokens (fp32 FMAs).  One thread per (b, t, which, h, c); grid
+// (D / 256, B * T0 * 3).  The H = 16 source values and coefficients are all loaded up front.
+__global__ __launch_bounds__(256) void early_mix_kernel(ProjArgs pa) {
+  constexpr int H = kFusedH;
+  const int d = pa.d, D = pa.D, P = pa.P, R = pa.R, T0 = pa.T0;
+  const int hc = blockIdx.x * 256 + threadIdx.x;
+  const int which = blockIdx.y % 3, bt = blockIdx.y / 3;
+  const int t = bt % T0, b = bt / T0;
+  const int h = hc / d, c = hc % d;
+  const float* __restrict__ y = pa.Ye + static_cast<int64_t>(bt) * 3 * D + which * D + c * H;
+  const float* __restrict__ al = pa.alpha[which];
+  float ym[H];
+#pragma unroll
+  for (int q = 0; q < H / 4; ++q) {
+    const floatx4 v = *reinterpret_cast<const floatx4*>(y + 4 * q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ym[4 * q + e] = v[e];
+  }
+  for (int j = 0; j < P; ++j) {
+    const int i = t * P + j;
+    if (i >= R) break;
+    float a[H];
+#pragma unroll
+    for (int m = 0; m < H; ++m) a[m] = al[(m * H + h) * P + j];
+    float acc = 0.f;
+#pragma unroll
+    for (int m = 0; m < H; ++m) acc = fmaf(a[m], ym[m], acc);
+    if (which == 2) pa.Vte[(static_cast<int64_t>(b * H + h) * d + c) * R + i] = acc;
+    else (which == 0 ? pa.Qe : pa.Ke)[(static_cast<int64_t>(b) * R + i) * D + h * d + c] = acc;
+  }
+}
+
+bool proj_fused(const ProjArgs& pa) { return fused_shape(pa.H, pa.D, pa.P); }
+
 hipError_t launch_proj_bf16(const ProjArgs& pa, hipStream_t s, hipEvent_t ev_prep, hipEvent_t ev_gemm) {
   const int D = pa.D, M = pa.B * pa.N;
-  hipLaunchKernelGGL(wprep_kernel, dim3(D / 64, D / 64, 3), dim3(256), 0, s, pa);
+  const bool fused = proj_fused(pa);
+  hipLaunchKernelGGL(wprep_kernel, dim3(D / 64, D / 64, 3), dim3(256), 0, s, pa, fused ? 1 : 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev_prep && (e = hipEventRecord(ev_prep, s)) != hipSuccess) return e;
+  if (fused) {
+    NtArgs g{};  // [Q~ K~ V~] = mix(Wt_perm * X^T)
+    g.A = pa.Wt;
+    g.B = pa.X;
+    g.I = 3 * D;
+    g.J = M;
+    g.K = D;
+    const int64_t tiles = static_cast<int64_t>(3 * D / GTI) * ((M + GTJ - 1) / GTJ);
+    if (static_cast<int64_t>(M) * D * 2 >= (int64_t{1} << 31) || static_cast<int64_t>(3) * D * D * 2 >= (int64_t{1} << 31))
+      return hipErrorInvalidValue;
+    switch (pa.P) {
+      case 1: hipLaunchKernelGGL((gemm_mix_bf16_kernel<1>), dim3(tiles), dim3(GThreads), 0, s, g, pa); break;
+      case 2: hipLaunchKernelGGL((gemm_mix_bf16_kernel<2>), dim3(tiles), dim3(GThreads), 0, s, g, pa); break;
+      default: hipLaunchKernelGGL((gemm_mix_bf16_kernel<4>), dim3(tiles), dim3(GThreads), 0, s, g, pa); break;
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (pa.R > 0) {
+      hipLaunchKernelGGL(early_mix_kernel, dim3(D / 256, pa.B * pa.T0 * 3), dim3(256), 0, s, pa);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    // the mixing step is part of the GEMM: both events mark its end
+    if (ev_gemm && (e = hipEventRecord(ev_gemm, s)) != hipSuccess) return e;
+    return hipSuccess;
+  }
   NtArgs g1{};  // Y_QK = X * Wt_QK^T
   g1.A = pa.X;
   g1.B = pa.Wt;
