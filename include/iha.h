@@ -109,6 +109,14 @@ typedef struct {
  * Validates the problem like iha_forward does. */
 iha_status iha_workspace_bytes(const iha_problem* prob, size_t* bytes);
 
+/* Which kernel path iha_forward takes for this problem: IHA_PLAN_* bits written
+ * to *plan (host-side only, no device work).  IHA_PLAN_MIX_FUSED: the pseudo-head
+ * mixing (Algorithm 1, step 2) runs in the epilogue of the projection GEMM, so no
+ * fp32 projections reach HBM and only the fp32 mixing of the first tokens is left
+ * as a separate mixing kernel.  Validates the problem like iha_forward does. */
+#define IHA_PLAN_MIX_FUSED 1u
+iha_status iha_plan(const iha_problem* prob, uint32_t* plan);
+
 /* The IHA forward pass (Algorithm 1) on `stream`.
  * X, W_Q, W_K, W_V: device, dtype prob->dtype.  alpha_*, R: device float.
  * X_out: device float [B][N][D].  workspace: device, >= iha_workspace_bytes(),
@@ -121,7 +129,8 @@ iha_status iha_forward(const iha_problem* prob, const void* X, const void* W_Q, 
 /* iha_forward that also records IHA_TIMED_EVENTS events on `stream` around its
  * steps: [0] start, [1] after the weight preparation (bf16: transpose; fp32:
  * mixing folded into the weights), [2] after the projection GEMMs, [3] after the
- * mixing (fp32: no separate mixing, recorded right after [2]), [4] after the
+ * mixing (fp32: no separate mixing, recorded right after [2]; IHA_PLAN_MIX_FUSED:
+ * only the fp32 mixing of the first tokens lies between [2] and [3]), [4] after the
  * attention kernel, [5] after the fp32 recomputation of the first stacked rows
  * (no work for IHA_F32 or IHA_MASK_NONE), [6] after the collapse.
  * The events are created by the caller (hipEventCreate) and must not be NULL;

@@ -18,6 +18,7 @@ STATUS_NAMES = ["IHA_OK", "IHA_ERR_INVALID_ARG", "IHA_ERR_SHAPE", "IHA_ERR_EMPTY
 IHA_MASK_NONE, IHA_MASK_CAUSAL, IHA_MASK_WINDOW = 0, 1, 2
 IHA_F32, IHA_BF16 = 0, 1
 IHA_FLAG_CHECK = 1
+IHA_PLAN_MIX_FUSED = 1
 TIMED_EVENTS = 7       # IHA_TIMED_EVENTS in include/iha.h
 _MASKS = {"none": IHA_MASK_NONE, "causal": IHA_MASK_CAUSAL, "window": IHA_MASK_WINDOW}
 
@@ -51,6 +52,8 @@ def load_library() -> ctypes.CDLL:
         lib.iha_workspace_bytes.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
         lib.iha_workspace_bytes.restype = ctypes.c_int
         fwd = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.iha_plan.argtypes = [P, ctypes.POINTER(ctypes.c_uint32)]
+        lib.iha_plan.restype = ctypes.c_int
         lib.iha_forward.argtypes = fwd
         lib.iha_forward.restype = ctypes.c_int
         lib.iha_forward_timed.argtypes = fwd + [ctypes.POINTER(vp)]
@@ -88,6 +91,15 @@ def iha_workspace_bytes(prob: iha_problem) -> int:
     st = load_library().iha_workspace_bytes(ctypes.byref(prob), ctypes.byref(n))
     if st != IHA_OK:
         raise IHAError(st, "iha_workspace_bytes")
+    return n.value
+
+
+def iha_plan(prob: iha_problem) -> int:
+    """IHA_PLAN_* bits: which kernel path iha_forward takes for `prob`."""
+    n = ctypes.c_uint32(0)
+    st = load_library().iha_plan(ctypes.byref(prob), ctypes.byref(n))
+    if st != IHA_OK:
+        raise IHAError(st, "iha_plan")
     return n.value
 
 

@@ -282,6 +282,14 @@ iha_status iha_workspace_bytes(const iha_problem* prob, size_t* bytes) {
   return IHA_OK;
 }
 
+iha_status iha_plan(const iha_problem* prob, uint32_t* plan) {
+  if (!plan) return IHA_ERR_INVALID_ARG;
+  const iha_status v = validate(prob);
+  if (v != IHA_OK) return v;
+  *plan = prob->dtype == IHA_BF16 && iha::fused_shape(prob->H, prob->D, prob->P) ? IHA_PLAN_MIX_FUSED : 0u;
+  return IHA_OK;
+}
+
 iha_status iha_forward(const iha_problem* prob, const void* X, const void* W_Q, const void* W_K,
                        const void* W_V, const float* alpha_Q, const float* alpha_K,
                        const float* alpha_V, const float* R, float* X_out, void* workspace,

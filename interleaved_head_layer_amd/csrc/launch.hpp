@@ -85,7 +85,8 @@ inline bool fused_shape(int64_t H, int64_t D, int64_t P) {
 // Q~ and K~ are then written in the chunked layout [B][H][d/8][P*N][8], else row-major.
 bool proj_fused(const ProjArgs& pa);
 // ev_prep (may be null) is recorded after the weight transpose, ev_gemm after the projection
-// GEMMs (with the fused path: after the fused kernel, the mixing included).
+// GEMMs (with the fused path: after the fused kernel, the mixing included, before the fp32
+// mixing of the first tokens).
 hipError_t launch_proj_bf16(const ProjArgs& pa, hipStream_t s, hipEvent_t ev_prep, hipEvent_t ev_gemm);
 
 // fp32 copies of the first R stacked rows (R = min(128, P*N)) of every (b, h) for bf16

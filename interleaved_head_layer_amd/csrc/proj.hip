@@ -44,12 +44,14 @@ __global__ __launch_bounds__(256) void wprep_kernel(ProjArgs pa, int cm) {
 // C[i][j] = sum_k A[i][k] * B[j][k]; A [I][K], B [J][K] bf16 (k contiguous), C fp32 with
 // row stride ldc; K a multiple of 64.  256 x 256 tiles, 8 waves as 2 x 4 (128 x 64 each:
 // every A fragment read from LDS feeds two matrix-core products, every B fragment four),
-// K slices of 64 in a two-stage LDS ring filled by buffer loads straight into LDS.  Rows
+// K slices of 64 in a two-stage LDS ring filled by buffer loads straight into LDS, register
+// fragments read one k-step ahead of the products that use them.  Rows
 // are 128 bytes with 16-byte chunks XOR-swizzled by (row >> 1) & 7, so the 16 lanes that
 // read 16 rows of one chunk hit 16 bank groups.  Rows past I / J read zero (buffer range
 // check) and their results are not stored.  The operands must each span < 2 GiB (the
 // launcher splits larger problems).
 constexpr int GTI = 256, GTJ = 256, GK = 64, GWaves = 8, GThreads = GWaves * 64;
+static_assert(GK == 64, "the main loop walks four k-steps of 16 per slice");
 
 __device__ __forceinline__ int gswz(int r) { return (r >> 1) & 7; }
 
@@ -98,6 +100,20 @@ __device__ __forceinline__ void gemm_tile(const NtArgs& g, NtSmem& sm, Epi&& epi
           static_cast<unsigned>((static_cast<int64_t>(j0 + 64 * p) * K + k0) * 2), 0, 0);
   };
 
+  // Per-lane LDS element offsets of the A / B fragments; k-step s reads chunk 2s + hf.
+  int ao[4], bo[2], asz[4], bsz[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wm * 128 + i * 32 + l32;
+    ao[i] = r * GK;
+    asz[i] = gswz(r);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = wn * 64 + j * 32 + l32;
+    bo[j] = r * GK;
+    bsz[j] = gswz(r);
+  }
   floatx16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -105,6 +121,31 @@ __device__ __forceinline__ void gemm_tile(const NtArgs& g, NtSmem& sm, Epi&& epi
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  // Fragments are read one k-step ahead into two register buffers (k-step s of a slice uses
+  // buffer s & 1), one LDS read between consecutive products; the products of a slice's last
+  // k-step are issued after the slice barrier, next to the first reads of the next slice.
+  bf16x8 fa[2][4], fb[2][2];
+  auto load = [&](int st, int s, int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      fa[buf][i] = *reinterpret_cast<const bf16x8*>(&sm.a[st][ao[i] + ((s * 2 + hf) ^ asz[i]) * 8]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      fb[buf][j] = *reinterpret_cast<const bf16x8*>(&sm.b[st][bo[j] + ((s * 2 + hf) ^ bsz[j]) * 8]);
+  };
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 6; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  };
 
   const int nk = K / GK;
   issue(0, 0);
@@ -113,28 +154,22 @@ __device__ __forceinline__ void gemm_tile(const NtArgs& g, NtSmem& sm, Epi&& epi
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
     if (kt + 1 < nk) issue((kt + 1) * GK, st ^ 1);  // the other stage was last read before the barrier
-#pragma unroll
-    for (int s = 0; s < GK / 16; ++s) {
-      bf16x8 af[4], bfr[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 128 + i * 32 + l32;
-        af[i] = *reinterpret_cast<const bf16x8*>(&sm.a[st][r * GK + ((s * 2 + hf) ^ gswz(r)) * 8]);
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = wn * 64 + j * 32 + l32;
-        bfr[j] = *reinterpret_cast<const bf16x8*>(&sm.b[st][r * GK + ((s * 2 + hf) ^ gswz(r)) * 8]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    load(st, 0, 0);
+    if (kt > 0) mma(1);
+    __builtin_amdgcn_sched_barrier(0);
+    load(st, 1, 1);
+    mma(0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(st, 2, 0);
+    mma(1);
+    __builtin_amdgcn_sched_barrier(0);
+    load(st, 3, 1);
+    mma(0);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();
   }
+  mma(1);
   epi(acc, i0, j0, wm, wn);
 }
 
@@ -231,31 +266,48 @@ __global__ __launch_bounds__(GThreads, 1) void gemm_mix_bf16_kernel(NtArgs g, Pr
         }
       }
       if (which < 2) {
-        // Q~ / K~: a lane gathers 4 of its 8 channels of each row (half of a 16-byte chunk)
-        // at a time, to bound the registers held next to the accumulators.
+        // Q~ / K~: with one block of 32 output rows (P <= 2) a lane gathers its 8 channels of
+        // each row, one whole 16-byte chunk per store; with more (P = 4) half a chunk at a
+        // time, to bound the registers held next to the accumulators.
         half_t* __restrict__ qk = which == 0 ? pa.Q : pa.K;
         const float oscale = which == 0 ? pa.qscale : 1.f;  // Q leaves pre-scaled, one rounding
         half_t* dst = qk + (static_cast<int64_t>(b * H) * (d / 8) + c0 / 8) * L * 8 + static_cast<int64_t>(t) * P * 8;
+        if constexpr (MB == 1) {
+          half8 stg[16];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+          for (int cl = 0; cl < 8; ++cl) {
+            const floatx16 o = mix_block<MB>(acc[cl >> 1][j], cl & 1, ah[0], alo[0]);
 #pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            half4 stg[16];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int cl = 4 * half + q;
-              const floatx16 o = mix_block<MB>(acc[cl >> 1][j], cl & 1, ah[mb], alo[mb]);
-#pragma unroll
-              for (int r = 0; r < 16; ++r) stg[r][q] = static_cast<half_t>(o[r] * oscale);
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int row = mb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-              if (ok && row < HP)
-                *reinterpret_cast<half4*>(dst + static_cast<int64_t>(row / P) * (d / 8) * L * 8 + (row % P) * 8 + 4 * half) =
-                    stg[r];
-            }
+            for (int r = 0; r < 16; ++r) stg[r][cl] = static_cast<half_t>(o[r] * oscale);
           }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (ok && row < HP)
+              *reinterpret_cast<half8*>(dst + static_cast<int64_t>(row / P) * (d / 8) * L * 8 + (row % P) * 8) = stg[r];
+          }
+        } else {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              half4 stg[16];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int cl = 4 * half + q;
+                const floatx16 o = mix_block<MB>(acc[cl >> 1][j], cl & 1, ah[mb], alo[mb]);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) stg[r][q] = static_cast<half_t>(o[r] * oscale);
+              }
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int row = mb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+                if (ok && row < HP)
+                  *reinterpret_cast<half4*>(dst + static_cast<int64_t>(row / P) * (d / 8) * L * 8 + (row % P) * 8 +
+                                            4 * half) = stg[r];
+              }
+            }
+        }
       } else {
         // V~^T: P consecutive fp16 per lane and head.
         typedef _Float16 halfp __attribute__((ext_vector_type(P)));
@@ -678,12 +730,13 @@ hipError_t launch_proj_bf16(const ProjArgs& pa, hipStream_t s, hipEvent_t ev_pre
       default: hipLaunchKernelGGL((gemm_mix_bf16_kernel<4>), dim3(tiles), dim3(GThreads), 0, s, g, pa); break;
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    // the mixing is part of the GEMM; what is left of the mixing step is the fp32 mixing
+    // of the first tokens
+    if (ev_gemm && (e = hipEventRecord(ev_gemm, s)) != hipSuccess) return e;
     if (pa.R > 0) {
       hipLaunchKernelGGL(early_mix_kernel, dim3(D / 256, pa.B * pa.T0 * 3), dim3(256), 0, s, pa);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    // the mixing step is part of the GEMM: both events mark its end
-    if (ev_gemm && (e = hipEventRecord(ev_gemm, s)) != hipSuccess) return e;
     return hipSuccess;
   }
   NtArgs g1{};  // Y_QK = X * Wt_QK^T

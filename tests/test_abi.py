@@ -23,7 +23,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = bd.load_library()
     names = declared_functions()
     assert {"iha_forward", "iha_workspace_bytes", "iha_status_str", "iha_attention",
-            "iha_forward_timed"} <= set(names)
+            "iha_forward_timed", "iha_plan"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -51,6 +51,43 @@ def test_workspace_size_covers_the_intermediates():
     assert need <= n <= need + 16 * 256
     st, n_none = _ws(mask="none")
     assert st == bd.IHA_OK and n_none < need - 3 * B * R * D * 4 + 16 * 256
+
+
+@pytest.mark.parametrize("B,N,D,H,P,dtype,fused", [
+    (4, 4096, 2048, 16, 2, bd.IHA_BF16, True),     # 16 heads of 128, P in {1, 2, 4}
+    (2, 256, 1024, 16, 4, bd.IHA_BF16, True),
+    (2, 256, 1024, 16, 1, bd.IHA_BF16, True),
+    (2, 256, 1024, 16, 3, bd.IHA_BF16, False),     # P = 3
+    (2, 8192, 2560, 20, 4, bd.IHA_BF16, False),    # H = 20
+    (2, 256, 1024, 16, 2, bd.IHA_F32, False),      # fp32 folds the mixing into the weights
+])
+def test_plan_and_workspace_follow_the_fused_mixing(B, N, D, H, P, dtype, fused):
+    """IHA_PLAN_MIX_FUSED is set exactly for bf16 with 16 heads, D a multiple of 256 and
+    P in {1, 2, 4}; then the workspace holds no fp32 projections of all tokens."""
+    p = bd.make_problem(B, N, D, H, P, "causal", None, dtype)
+    assert bd.iha_plan(p) == (bd.IHA_PLAN_MIX_FUSED if fused else 0)
+    n = bd.iha_workspace_bytes(p)
+    stacked = 3 * B * P * N * D * 2 + B * P * N * D * 4           # Q~ K~ V~^T, P-bar
+    if dtype == bd.IHA_BF16:
+        stacked += 3 * D * D * 2                                  # transposed weights
+    if dtype == bd.IHA_BF16:                                      # fp32 first rows (causal)
+        R = min(128, P * N)
+        stacked += 3 * B * R * D * 4
+        if fused:
+            stacked += B * -(-R // P) * 3 * D * 4                 # their unmixed projections
+    fp32_proj = B * N * 3 * D * 4
+    if fused:
+        assert stacked <= n <= stacked + 16 * 256
+    elif dtype == bd.IHA_BF16:
+        assert stacked + fp32_proj <= n <= stacked + fp32_proj + 16 * 256
+
+
+def test_plan_validates():
+    st = bd.load_library().iha_plan(ctypes.byref(bd.make_problem(0, 64, 128, 2, 2, "causal")),
+                                    ctypes.byref(ctypes.c_uint32()))
+    assert st == bd.STATUS_NAMES.index("IHA_ERR_INVALID_ARG")
+    assert bd.load_library().iha_plan(ctypes.byref(bd.make_problem(1, 64, 128, 2, 2, "causal")),
+                                      None) == bd.STATUS_NAMES.index("IHA_ERR_INVALID_ARG")
 
 
 @pytest.mark.parametrize("kw,code", [
