@@ -213,8 +213,10 @@ def main():
             extra[name] = {"ms_per_step": round(e["ms_step"], 4),
                            "pseudo_tokens_per_s": round(e["value"], 1),
                            "attention": dict(e["roofs"]["attention"],
-                                             ms=round(e["kms"]["attention"], 4)),
-                           "gemm": e["roofs"]["gemm"], "mix_fused": e["mix_fused"],
+                                             ms=round(e["kms"]["attention"], 4),
+                                             traffic=counter_traffic(name, "attention")),
+                           "gemm": dict(e["roofs"]["gemm"], traffic=counter_traffic(name, "gemm")),
+                           "mix_fused": e["mix_fused"],
                            "kernels_ms": {k: round(v, 4) for k, v in e["kms"].items()}}
 
     line = {
