@@ -118,9 +118,11 @@ iha_status iha_workspace_bytes(const iha_problem* prob, size_t* bytes);
 iha_status iha_plan(const iha_problem* prob, uint32_t* plan);
 
 /* The IHA forward pass (Algorithm 1) on `stream`.
- * X, W_Q, W_K, W_V: device, dtype prob->dtype.  alpha_*, R: device float.
- * X_out: device float [B][N][D].  workspace: device, >= iha_workspace_bytes(),
- * 256-byte aligned. */
+ * X, W_Q, W_K, W_V: device, dtype prob->dtype, 16-byte aligned.  alpha_*, R:
+ * device float.  X_out: device float [B][N][D], 16-byte aligned.  workspace:
+ * device, >= iha_workspace_bytes(), 256-byte aligned.  A misaligned X, W_*, X_out,
+ * alpha_* or R returns IHA_ERR_INVALID_ARG, a misaligned workspace
+ * IHA_ERR_WORKSPACE, before any launch. */
 iha_status iha_forward(const iha_problem* prob, const void* X, const void* W_Q, const void* W_K,
                        const void* W_V, const float* alpha_Q, const float* alpha_K,
                        const float* alpha_V, const float* R, float* X_out, void* workspace,
@@ -147,6 +149,7 @@ iha_status iha_forward_timed(const iha_problem* prob, const void* X, const void*
  *   Q, K   fp16 [B][L][H][d]   (row i = stacked position i)
  *   Vt     fp16 [B][H][d][L]   (values, channel-major)
  *   O      float [B][L][H][d]  O[i] = sum_{i' visible} softmax_i'(s) V[i']
+ * (all four device pointers 16-byte aligned, else IHA_ERR_INVALID_ARG)
  * with scores s = (q_i . k_i') * score_scale.  The kernel works in base 2, so
  * pass score_scale = log2(e)/sqrt(d) for the textbook's softmax(QK^T/sqrt(d)).
  * mask/window as above on i.  d must be 64 or 128.  IHA_FLAG_CHECK in

@@ -311,7 +311,8 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
 
   // Q fragments: all loads in flight at once (rows past the end read the last row, whose
   // results are never stored), then the first K/V tile, then the optional scale.
-  const int qrow = q0 + w * 32 + l32;
+  const int r0 = q0 + w * 32;  // the wave's first row (wave-uniform)
+  const int qrow = r0 + l32;
   const int qload = min(qrow, L - 1);
   half8 qf[NKS];
 #pragma unroll
@@ -356,11 +357,18 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
     const bool more = kt + 1 < kt1;
     // The other stage was last read before the previous barrier: refill it now.
     if (more) cp.issue(Kb, Vb, k0 + ABN, sm.k[stage ^ 1], sm.v[stage ^ 1]);
-    // Only tiles that cross a mask edge or the end of the sequence test keys.
-    bool edge = (k0 + ABN > L);
-    if (MASK != kMaskNone) edge |= (k0 + ABN - 1 > q0);
-    if (MASK == kMaskWindow) edge |= (k0 <= q0 + ABM - 1 - window);
-    attn_tile<DH, MASK>(edge, sm.k[stage], sm.v[stage], qf, st, negm, k0, qrow, L, window, krow, l32, hf);
+    // A wave skips tiles that hold no visible key for any of its 32 rows; only tiles that
+    // cross a mask edge (for its rows) or the end of the sequence test keys.
+    bool edge = (k0 + ABN > L), act = true;
+    if (MASK != kMaskNone) {
+      act = k0 <= r0 + 31;
+      edge |= (k0 + ABN - 1 > r0);
+    }
+    if (MASK == kMaskWindow) {
+      act = act && (k0 + ABN - 1 > r0 - window);
+      edge |= (k0 <= r0 + 31 - window);
+    }
+    if (act) attn_tile<DH, MASK>(edge, sm.k[stage], sm.v[stage], qf, st, negm, k0, qrow, L, window, krow, l32, hf);
     if (more) cp.commit(sm.k[stage ^ 1], sm.v[stage ^ 1]);
     wait_global_loads();
     __syncthreads();

@@ -19,6 +19,7 @@ constexpr int64_t kMaxRows = int64_t(1) << 30;   // B*N tokens and P*N stacked r
 constexpr int64_t kMaxElems = int64_t(1) << 40;  // elements of any one tensor
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
 struct Layout {
   size_t flag, wt, yqk, yvt, ye, q, k, vt, pbar, qe, ke, vte, total;
@@ -127,6 +128,11 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
   const iha_status v = validate(prob);
   if (v != IHA_OK) return v;
   if (!X || !W_Q || !W_K || !W_V || !alpha_Q || !alpha_K || !alpha_V || !R || !X_out)
+    return IHA_ERR_INVALID_ARG;
+  // The kernels move X, W and X_out in 16-byte vectors and alpha, R as floats.
+  if (!aligned(X, 16) || !aligned(W_Q, 16) || !aligned(W_K, 16) || !aligned(W_V, 16) ||
+      !aligned(X_out, 16) || !aligned(alpha_Q, 4) || !aligned(alpha_K, 4) || !aligned(alpha_V, 4) ||
+      !aligned(R, 4))
     return IHA_ERR_INVALID_ARG;
   const iha_problem& p = *prob;
   const Layout lay = layout_of(p);
@@ -317,6 +323,7 @@ iha_status iha_attention(int64_t B, int64_t L, int64_t H, int64_t d, int32_t mas
     return IHA_ERR_INVALID_ARG;
   if (!Q || !K || !Vt || !O || !(score_scale > 0.f) || !std::isfinite(score_scale))
     return IHA_ERR_INVALID_ARG;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(Vt, 16) || !aligned(O, 16)) return IHA_ERR_INVALID_ARG;
   if ((flags & ~IHA_FLAG_CHECK) != 0) return IHA_ERR_INVALID_ARG;
   if ((flags & IHA_FLAG_CHECK) && !flag_buf) return IHA_ERR_WORKSPACE;
   if (d != 64 && d != 128) return IHA_ERR_UNSUPPORTED;

@@ -20,23 +20,39 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // ------------------------------------------------------------------- W transpose
-// grid: (D/64, D/64, 3); block 256.  64x64 tiles through LDS.  With `cm`, column n = m*d + c
-// of W (head m, channel c) goes to row c*H + m instead of row n (the fused mixing wants the H
-// source heads of a channel in consecutive rows).
+// grid: (D/64, D/64, 3); block 256.  64x64 tiles through LDS, 16-byte global loads and
+// stores (8 bf16 per thread and access).  With `cm`, column n = m*d + c of W (head m,
+// channel c) goes to row c*H + m instead of row n (the fused mixing wants the H source
+// heads of a channel in consecutive rows).
 __global__ __launch_bounds__(256) void wprep_kernel(ProjArgs pa, int cm) {
-  __shared__ uint16_t t[64][65];
+  __shared__ uint16_t t[64][64 + 2];  // [k][n]; the pad staggers the column reads
   const int which = blockIdx.z;
   const uint16_t* __restrict__ W = pa.W[which];
   const int D = pa.D, d = pa.d, H = pa.H;
   const int k0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
-  const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;
-  for (int r = ty; r < 64; r += 4) t[r][tx] = W[static_cast<int64_t>(k0 + r) * D + n0 + tx];
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {  // 64 rows of 8 x 16 bytes
+    const int x = tid + 256 * q, r = x >> 3, c8 = (x & 7) * 8;
+    const uint4 v = *reinterpret_cast<const uint4*>(W + static_cast<int64_t>(k0 + r) * D + n0 + c8);
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      t[r][c8 + 2 * e] = static_cast<uint16_t>(w4[e] & 0xFFFFu);
+      t[r][c8 + 2 * e + 1] = static_cast<uint16_t>(w4[e] >> 16);
+    }
+  }
   __syncthreads();
   uint16_t* __restrict__ Wt = pa.Wt + static_cast<int64_t>(which) * D * D;
-  for (int r = ty; r < 64; r += 4) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {  // 64 output rows (n) of 8 x 16 bytes (k)
+    const int x = tid + 256 * q, r = x >> 3, k8 = (x & 7) * 8;
     const int n = n0 + r;
     const int row = cm ? (n % d) * H + n / d : n;
-    Wt[static_cast<int64_t>(row) * D + k0 + tx] = t[tx][r];
+    uint32_t w4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w4[e] = static_cast<uint32_t>(t[k8 + 2 * e][r]) | (static_cast<uint32_t>(t[k8 + 2 * e + 1][r]) << 16);
+    *reinterpret_cast<uint4*>(Wt + static_cast<int64_t>(row) * D + k0 + k8) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
   }
 }
 

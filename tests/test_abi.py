@@ -121,6 +121,14 @@ def test_forward_rejects_before_any_launch():
     st = lib.iha_forward(ctypes.byref(p), *args[:8], fake, ctypes.c_void_p(4096 + 8),
                          ctypes.c_size_t(1 << 40), None)
     assert st == bd.STATUS_NAMES.index("IHA_ERR_WORKSPACE")     # misaligned
+    odd = ctypes.c_void_p(4096 + 8)                               # 8-byte, not 16-byte aligned
+    for k in (0, 1, 8):                                           # X, W_Q, X_out
+        a = list(args[:8]) + [fake]
+        a[k] = odd
+        st = lib.iha_forward(ctypes.byref(p), *a, fake, ctypes.c_size_t(1 << 40), None)
+        assert st == bd.STATUS_NAMES.index("IHA_ERR_INVALID_ARG"), k
+    st = lib.iha_attention(1, 64, 2, 128, 0, 0, 1.0, fake, odd, fake, fake, 0, None, None)
+    assert st == bd.STATUS_NAMES.index("IHA_ERR_INVALID_ARG")
     st = lib.iha_attention(1, 64, 2, 96, 0, 0, 1.0, fake, fake, fake, fake, 0, None, None)
     assert st == bd.STATUS_NAMES.index("IHA_ERR_UNSUPPORTED")
     st = lib.iha_attention(1, 64, 2, 128, 2, 0, 1.0, fake, fake, fake, fake, 0, None, None)
