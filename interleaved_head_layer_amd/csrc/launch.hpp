@@ -78,10 +78,14 @@ struct ProjArgs {
   int T0;                 // ceil(R / P): tokens whose pseudo-tokens include a first row
   float qscale;           // factor applied to the fp16 Q (the base-2 score scale)
 };
+// With P = 4 the fused epilogue writes four stacked outputs per projected value and its
+// stores no longer hide behind the products (measured: slower than GEMM + mixing), so the
+// fused path stops at P = 2.
 inline bool fused_shape(int64_t H, int64_t D, int64_t P) {
-  return H == 16 && D % 256 == 0 && (P == 1 || P == 2 || P == 4);
+  return ((H == 16 && D % 256 == 0) || (H == 20 && D % 320 == 0)) && (P == 1 || P == 2);
 }
-// True when the projection runs fused with the mixing (H = 16, D % 256 == 0, P in {1,2,4});
+// True when the projection runs fused with the mixing (H = 16 with D % 256 == 0 or H = 20
+// with D % 320 == 0, P in {1,2});
 // Q~ and K~ are then written in the chunked layout [B][H][d/8][P*N][8], else row-major.
 bool proj_fused(const ProjArgs& pa);
 // ev_prep (may be null) is recorded after the weight transpose, ev_gemm after the projection

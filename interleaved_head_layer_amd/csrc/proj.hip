@@ -19,11 +19,18 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
+// Row of (channel c, source head m) of one weight matrix in the fused layout (H = 16 or 20):
+// 8-channel groups of 8H rows; in a group, channel cl's heads m < 16 at rows cl*16 + m and
+// (H = 20) its heads 16..19 at rows 128 + cl*4 + (m - 16).
+__device__ __forceinline__ int fused_row(int c, int m, int H) {
+  return (c >> 3) * (8 * H) + (m < 16 ? (c & 7) * 16 + m : 128 + (c & 7) * 4 + (m - 16));
+}
+
 // ------------------------------------------------------------------- W transpose
 // grid: (D/64, D/64, 3); block 256.  64x64 tiles through LDS, 16-byte global loads and
 // stores (8 bf16 per thread and access).  With `cm`, column n = m*d + c of W (head m,
-// channel c) goes to row c*H + m instead of row n (the fused mixing wants the H source
-// heads of a channel in consecutive rows).
+// channel c) goes to row fused_row(c, m) instead of row n (the fused mixing wants the
+// source heads of 8 channels in one wave's rows).
 __global__ __launch_bounds__(256) void wprep_kernel(ProjArgs pa, int cm) {
   __shared__ uint16_t t[64][64 + 2];  // [k][n]; the pad staggers the column reads
   const int which = blockIdx.z;
@@ -48,7 +55,7 @@ __global__ __launch_bounds__(256) void wprep_kernel(ProjArgs pa, int cm) {
   for (int q = 0; q < 2; ++q) {  // 64 output rows (n) of 8 x 16 bytes (k)
     const int x = tid + 256 * q, r = x >> 3, k8 = (x & 7) * 8;
     const int n = n0 + r;
-    const int row = cm ? (n % d) * H + n / d : n;
+    const int row = cm ? fused_row(n % d, n / d, H) : n;
     uint32_t w4[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) w4[e] = static_cast<uint32_t>(t[k8 + 2 * e][r]) | (static_cast<uint32_t>(t[k8 + 2 * e + 1][r]) << 16);
@@ -58,8 +65,9 @@ __global__ __launch_bounds__(256) void wprep_kernel(ProjArgs pa, int cm) {
 
 // ------------------------------------------------------------------- NT GEMM
 // C[i][j] = sum_k A[i][k] * B[j][k]; A [I][K], B [J][K] bf16 (k contiguous), C fp32 with
-// row stride ldc; K a multiple of 64.  256 x 256 tiles, 8 waves as 2 x 4 (128 x 64 each:
-// every A fragment read from LDS feeds two matrix-core products, every B fragment four),
+// row stride ldc; K a multiple of 64.  TI x 256 tiles (TI = 64 RBW: 256, or 320 for the
+// fused mixing with 20 heads), 8 waves as 2 x 4 (32 RBW x 64 each: every A fragment read
+// from LDS feeds two matrix-core products, every B fragment RBW),
 // K slices of 64 in a two-stage LDS ring filled by buffer loads straight into LDS, register
 // fragments read one k-step ahead of the products that use them.  Rows
 // are 128 bytes with 16-byte chunks XOR-swizzled by (row >> 1) & 7, so the 16 lanes that
@@ -67,20 +75,23 @@ __global__ __launch_bounds__(256) void wprep_kernel(ProjArgs pa, int cm) {
 // check) and their results are not stored.  The operands must each span < 2 GiB (the
 // launcher splits larger problems).
 constexpr int GTI = 256, GTJ = 256, GK = 64, GWaves = 8, GThreads = GWaves * 64;
+constexpr int GRBW = GTI / 64;  // 32-row blocks per wave of the plain GEMM
 static_assert(GK == 64, "the main loop walks four k-steps of 16 per slice");
 
 __device__ __forceinline__ int gswz(int r) { return (r >> 1) & 7; }
 
+template <int RBW>
 struct NtSmem {
-  uint16_t a[2][GTI * GK];
+  uint16_t a[2][64 * RBW * GK];
   uint16_t b[2][GTJ * GK];
 };
 
-// Main loop of one 256 x 256 tile; hands the accumulators to epi(acc, i0, j0, wm, wn).
-template <typename Epi>
-__device__ __forceinline__ void gemm_tile(const NtArgs& g, NtSmem& sm, Epi&& epi) {
+// Main loop of one (64 RBW) x 256 tile; hands the accumulators to epi(acc, i0, j0, wm, wn).
+template <int RBW, typename Epi>
+__device__ __forceinline__ void gemm_tile(const NtArgs& g, NtSmem<RBW>& sm, Epi&& epi) {
+  constexpr int TI = 64 * RBW;
   const int I = g.I, J = g.J, K = g.K;
-  const int ntj = (J + GTJ - 1) / GTJ, nti = (I + GTI - 1) / GTI;
+  const int ntj = (J + GTJ - 1) / GTJ, nti = (I + TI - 1) / TI;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   // Groups of 4 row tiles sweep the column tiles, so a group's A slices stay in L2.
   constexpr int GR = 4;
@@ -89,7 +100,7 @@ __device__ __forceinline__ void gemm_tile(const NtArgs& g, NtSmem& sm, Epi&& epi
   const int gsize = min(GR, nti - first_i);
   const int ti = first_i + (lid % (GR * ntj)) % gsize;
   const int tj = (lid % (GR * ntj)) / gsize;
-  const int i0 = ti * GTI, j0 = tj * GTJ;
+  const int i0 = ti * TI, j0 = tj * GTJ;
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -105,7 +116,7 @@ __device__ __forceinline__ void gemm_tile(const NtArgs& g, NtSmem& sm, Epi&& epi
   const unsigned loff = static_cast<unsigned>((rl * K + (pos ^ gswz(rl)) * 8) * 2);
   auto issue = [&](int k0, int st) {
 #pragma unroll
-    for (int p = 0; p < GTI / 64; ++p)
+    for (int p = 0; p < TI / 64; ++p)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ra, (__attribute__((address_space(3))) void*)(sm.a[st] + (p * GWaves + wave) * 512), 16, loff,
           static_cast<unsigned>((static_cast<int64_t>(i0 + 64 * p) * K + k0) * 2), 0, 0);
@@ -117,10 +128,10 @@ __device__ __forceinline__ void gemm_tile(const NtArgs& g, NtSmem& sm, Epi&& epi
   };
 
   // Per-lane LDS element offsets of the A / B fragments; k-step s reads chunk 2s + hf.
-  int ao[4], bo[2], asz[4], bsz[2];
+  int ao[RBW], bo[2], asz[RBW], bsz[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = wm * 128 + i * 32 + l32;
+  for (int i = 0; i < RBW; ++i) {
+    const int r = wm * 32 * RBW + i * 32 + l32;
     ao[i] = r * GK;
     asz[i] = gswz(r);
   }
@@ -130,9 +141,9 @@ __device__ __forceinline__ void gemm_tile(const NtArgs& g, NtSmem& sm, Epi&& epi
     bo[j] = r * GK;
     bsz[j] = gswz(r);
   }
-  floatx16 acc[4][2];
+  floatx16 acc[RBW][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < RBW; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -140,10 +151,10 @@ __device__ __forceinline__ void gemm_tile(const NtArgs& g, NtSmem& sm, Epi&& epi
   // Fragments are read one k-step ahead into two register buffers (k-step s of a slice uses
   // buffer s & 1), one LDS read between consecutive products; the products of a slice's last
   // k-step are issued after the slice barrier, next to the first reads of the next slice.
-  bf16x8 fa[2][4], fb[2][2];
+  bf16x8 fa[2][RBW], fb[2][2];
   auto load = [&](int st, int s, int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < RBW; ++i)
       fa[buf][i] = *reinterpret_cast<const bf16x8*>(&sm.a[st][ao[i] + ((s * 2 + hf) ^ asz[i]) * 8]);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -151,16 +162,16 @@ __device__ __forceinline__ void gemm_tile(const NtArgs& g, NtSmem& sm, Epi&& epi
   };
   auto mma = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < RBW; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
 #pragma unroll
-    for (int q = 0; q < 6; ++q) {
+    for (int q = 0; q < RBW + 2; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * RBW - (RBW + 2), 0);
   };
 
   const int nk = K / GK;
@@ -190,13 +201,13 @@ __device__ __forceinline__ void gemm_tile(const NtArgs& g, NtSmem& sm, Epi&& epi
 }
 
 __global__ __launch_bounds__(GThreads, 1) void gemm_nt_bf16_kernel(NtArgs g) {
-  __shared__ __attribute__((aligned(16))) NtSmem sm;
-  gemm_tile(g, sm, [&](floatx16 (&acc)[4][2], int i0, int j0, int wm, int wn) {
+  __shared__ __attribute__((aligned(16))) NtSmem<GRBW> sm;
+  gemm_tile<GRBW>(g, sm, [&](floatx16 (&acc)[GRBW][2], int i0, int j0, int wm, int wn) {
     const int lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5;
     const int I = g.I, J = g.J;
     // Lane l holds C[8*(r/4) + 4*hf + r%4][l%32] of each 32x32 block.
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < GRBW; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int col = j0 + wn * 64 + j * 32 + l32;
@@ -211,88 +222,175 @@ __global__ __launch_bounds__(GThreads, 1) void gemm_nt_bf16_kernel(NtArgs g) {
 }
 
 // ------------------------------------------------------------------- fused projection + mixing
-// For H = 16 the weight rows are permuted to (which, c, m) (wprep with cm), so each 32-row
-// block of a tile holds the 16 source heads of two channels and a lane's accumulator
-// registers 0..7 (8..15) are 8 of the 16 source heads of the first (second) channel for one
-// token: exactly the B operand of a 32x32x16 product over the source heads, with k-slot
-// 8*hf + e standing for head m = 8*(e/4) + 4*hf + e%4.  The epilogue mixes in place
+// For H = 16 and H = 20 the weight rows of each matrix are permuted (wprep with cm) so that
+// a wave's 32*RBW rows are the H source heads of 8 consecutive channels (RBW = H / 4 blocks
+// of 32 rows):
+//   rows cl*16 + m        (m < 16):  "main" blocks, two channels of 16 source heads each;
+//   rows 128 + cl*4 + m-16 (m >= 16, H = 20): one "rest" block, 8 channels x 4 heads.
+// A lane's accumulator registers 0..7 (8..15) of a block are rows 8*(e/4) + 4*hf + e%4 of
+// its first (second) half: exactly the B operand of a 32x32x16 product whose k-slot
+// 8*hf + e stands for that row.  The epilogue mixes in place
 //   out[(h, j)][token] = sum_m alpha[m][h][j] * Y[(c, m)][token]
-// with the fp16 hi/lo split (three products, fp32 accumulation, ~2^-21 relative) and writes
+// as alpha^T (A operand, 32 rows (h, j) per block) times the main half of channel c, plus
+// (H = 20) alpha^T of heads 16..19, zero outside channel c's four k-slots, times the rest
+// half that holds c.  Both operands are split into fp16 hi + lo (three products per pair,
+// fp32 accumulation, ~2^-21 relative).  Outputs:
 //   V~^T [B][H][d][P*N]           (P consecutive fp16 per lane and head),
 //   Q~, K~ [B][H][d/8][P*N][8]    (a wave's 8 channels form one 16-byte chunk per row),
-// plus the fp32 first rows; the fp32 projections never reach HBM.
-constexpr int kFusedH = 16;
-
-// mix(o): the mixed values of one channel for one 32-token column block: lane row r is
-// (h, jj) with h*P + jj = mb*32 + 8*(r/4) + 4*hf + r%4, column = the lane's token.
-template <int MB>
-__device__ __forceinline__ floatx16 mix_block(const floatx16& y, int cs, const half8& ah, const half8& alo) {
-  half8 bh, bl;
+// plus the unmixed fp32 projections of the first tokens (mixed by early_mix_kernel); the
+// fp32 projections of all tokens never reach HBM.
+__device__ __forceinline__ void split_f16(const floatx16& y, int cs, half8& bh, half8& bl) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float x = y[8 * cs + e];
     bh[e] = static_cast<half_t>(x);
     bl[e] = static_cast<half_t>(x - static_cast<float>(bh[e]));
   }
+}
+
+// Mixed values of channel cl (0..7 within the wave) for one 32-token column block: lane row
+// r is (h, jj) with h*P + jj = mb*32 + 8*(r/4) + 4*hf + r%4, column = the lane's token.
+// yh/yl: the fp16 hi/lo B operands of the wave's accumulator block halves of this column
+// block ([block][half]); ah/alo: alpha^T of heads 0..15; arh/arl (H = 20): alpha^T of heads
+// 16..19 in both element groups.
+template <int H, int RBW>
+__device__ __forceinline__ floatx16 mix_channel(const half8 (&yh)[RBW][2], const half8 (&yl)[RBW][2], int cl, int hf,
+                                                const half8& ah, const half8& alo, const half8& arh,
+                                                const half8& arl) {
   floatx16 o;
 #pragma unroll
   for (int r = 0; r < 16; ++r) o[r] = 0.f;
+  const half8& bh = yh[cl >> 1][cl & 1];
+  const half8& bl = yl[cl >> 1][cl & 1];
   o = mfma32(ah, bh, o);
   o = mfma32(alo, bh, o);
-  return mfma32(ah, bl, o);
+  o = mfma32(ah, bl, o);
+  if constexpr (H == 20) {
+    // Rest half cl / 4; k-slot 8*hf + e holds channel 4*(cl/4) + 2*(e/4) + hf: keep the
+    // element group whose channel is cl.
+    const half8& rbh = yh[4][cl >> 2];
+    const half8& rbl = yl[4][cl >> 2];
+    const int ct = cl & 3;
+    const bool g0 = ct == hf, g1 = ct == 2 + hf;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 h4 = __builtin_bit_cast(u32x4, arh), l4 = __builtin_bit_cast(u32x4, arl);
+    h4[0] = g0 ? h4[0] : 0u;
+    h4[1] = g0 ? h4[1] : 0u;
+    h4[2] = g1 ? h4[2] : 0u;
+    h4[3] = g1 ? h4[3] : 0u;
+    l4[0] = g0 ? l4[0] : 0u;
+    l4[1] = g0 ? l4[1] : 0u;
+    l4[2] = g1 ? l4[2] : 0u;
+    l4[3] = g1 ? l4[3] : 0u;
+    const half8 rh = __builtin_bit_cast(half8, h4), rl = __builtin_bit_cast(half8, l4);
+    o = mfma32(rh, rbh, o);
+    o = mfma32(rl, rbh, o);
+    o = mfma32(rh, rbl, o);
+  } else {
+    (void)arh;
+    (void)arl;
+  }
+  return o;
 }
 
-template <int P>
+template <int H, int P>
 __global__ __launch_bounds__(GThreads, 1) void gemm_mix_bf16_kernel(NtArgs g, ProjArgs pa) {
-  __shared__ __attribute__((aligned(16))) NtSmem sm;
-  gemm_tile(g, sm, [&](floatx16 (&acc)[4][2], int i0, int j0, int wm, int wn) {
-    constexpr int H = kFusedH, HP = H * P, MB = (HP + 31) / 32;
+  constexpr int RBW = H / 4, HP = H * P, MB = (HP + 31) / 32;
+  __shared__ __attribute__((aligned(16))) NtSmem<RBW> sm;
+  gemm_tile<RBW>(g, sm, [&](floatx16 (&acc)[RBW][2], int i0, int j0, int wm, int wn) {
     const int lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5;
     const int D = pa.D, d = pa.d, N = pa.N, M = g.J;
-    const int which = i0 / D;                       // tiles never straddle Q / K / V
-    const int c0 = ((i0 % D) + 128 * wm) / H;       // the wave's 8 channels: c0 .. c0 + 7
+    const int which = i0 / D;                          // tiles never straddle Q / K / V
+    const int c0 = ((i0 % D) + 32 * RBW * wm) / H;     // the wave's 8 channels: c0 .. c0 + 7
     const float* __restrict__ al = pa.alpha[which];
     const int64_t L = static_cast<int64_t>(P) * N;
-    half8 ah[MB], alo[MB];
+    // alpha^T operands: lane (row = mb*32 + l32, element e) holds alpha[m][row] for the head m
+    // of k-slot 8*hf + e: main m = 8*(e/4) + 4*hf + e%4, rest m = 16 + e%4.  With 20 heads
+    // all four kinds go to LDS (free after the main loop) and are read where used, to keep
+    // registers for the accumulators; with 16 the main ones stay in registers.
+    constexpr bool kLdsAlpha = H == 20;
+    half8 ah[kLdsAlpha ? 1 : MB], alo[kLdsAlpha ? 1 : MB];
+    half8* at = reinterpret_cast<half8*>(&sm);  // [kind: main hi, main lo, rest hi, rest lo][mb][lane]
+    auto alpha_op = [&](int kind, int mb, int row, int e) {
+      const int m = kind < 2 ? 8 * (e >> 2) + 4 * ((threadIdx.x & 63) >> 5) + (e & 3) : 16 + (e & 3);
+      return row < HP ? al[m * HP + row] : 0.f;
+    };
+    if constexpr (kLdsAlpha) {
+      for (int x = threadIdx.x; x < 2 * MB * 64; x += GThreads) {  // (rest?, mb, lane)
+        const int ln = x & 63, mb = (x >> 6) % MB, kind = 2 * (x / (64 * MB));
+        const int row = mb * 32 + (ln & 31), hfx = ln >> 5;
+        half8 vh, vl;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int row = mb * 32 + l32, m = 8 * (e >> 2) + 4 * hf + (e & 3);
-        const float v = al[row < HP ? m * HP + row : 0];
-        const float a = row < HP ? v : 0.f;
-        ah[mb][e] = static_cast<half_t>(a);
-        alo[mb][e] = static_cast<half_t>(a - static_cast<float>(ah[mb][e]));
+        for (int e = 0; e < 8; ++e) {
+          const int m = kind < 2 ? 8 * (e >> 2) + 4 * hfx + (e & 3) : 16 + (e & 3);
+          const float a = row < HP ? al[m * HP + row] : 0.f;
+          vh[e] = static_cast<half_t>(a);
+          vl[e] = static_cast<half_t>(a - static_cast<float>(vh[e]));
+        }
+        at[((kind + 0) * MB + mb) * 64 + ln] = vh;
+        at[((kind + 1) * MB + mb) * 64 + ln] = vl;
       }
+      __syncthreads();  // every wave finished its main loop before the LDS was rewritten
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float a = alpha_op(0, mb, mb * 32 + l32, e);
+          ah[mb][e] = static_cast<half_t>(a);
+          alo[mb][e] = static_cast<half_t>(a - static_cast<float>(ah[mb][e]));
+        }
+    }
+    // The first tokens' raw fp32 projections (rare column blocks holding a sequence's first
+    // T0 tokens) go to Ye[b][t][which*D + row] (row as permuted); early_mix_kernel mixes them
+    // into the fp32 first rows.
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int tok = j0 + 64 * wn + 32 * j + l32;
+      const int b = tok / N, t = tok % N;
+      if (__builtin_expect(__any(tok < M && t < pa.T0), false)) {
+        if (tok < M && t < pa.T0) {
+          float* ye = pa.Ye + (static_cast<int64_t>(b) * pa.T0 + t) * 3 * D + i0 + 32 * RBW * wm;
+#pragma unroll
+          for (int i = 0; i < RBW; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ye[32 * i + 8 * (r >> 2) + 4 * hf + (r & 3)] = acc[i][j][r];
+        }
+      }
+    }
+    // All accumulators become fp16 hi/lo B operands (the fp32 values are not needed again).
+    half8 yh[2][RBW][2], yl[2][RBW][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < RBW; ++i)
+#pragma unroll
+        for (int cs = 0; cs < 2; ++cs) split_f16(acc[i][j], cs, yh[j][i][cs], yl[j][i][cs]);
+    // mixed channel cl, column block j, output block mb
+    auto mixc = [&](int j, int cl, int mb) {
+      if constexpr (kLdsAlpha)
+        return mix_channel<H, RBW>(yh[j], yl[j], cl, hf, at[(0 * MB + mb) * 64 + lane], at[(1 * MB + mb) * 64 + lane],
+                                   at[(2 * MB + mb) * 64 + lane], at[(3 * MB + mb) * 64 + lane]);
+      else
+        return mix_channel<H, RBW>(yh[j], yl[j], cl, hf, ah[mb], alo[mb], ah[mb], alo[mb]);
+    };
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int tok = j0 + 64 * wn + 32 * j + l32;
       const bool ok = tok < M;
       const int b = tok / N, t = tok % N;
-      if (__builtin_expect(__any(ok && t < pa.T0), false)) {
-        // Rare column blocks holding a sequence's first T0 tokens: their unmixed fp32
-        // projections go to Ye[b][t][row] (row = which*D + c*H + m); a small kernel mixes them
-        // into the fp32 first rows.
-        if (ok && t < pa.T0) {
-          float* ye = pa.Ye + (static_cast<int64_t>(b) * pa.T0 + t) * 3 * D + i0 + 128 * wm;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) ye[32 * i + 8 * (r >> 2) + 4 * hf + (r & 3)] = acc[i][j][r];
-        }
-      }
       if (which < 2) {
-        // Q~ / K~: with one block of 32 output rows (P <= 2) a lane gathers its 8 channels of
-        // each row, one whole 16-byte chunk per store; with more (P = 4) half a chunk at a
-        // time, to bound the registers held next to the accumulators.
+        // Q~ / K~: with 16 heads and one block of 32 output rows (H*P <= 32) a lane gathers its
+        // 8 channels of each row, one whole 16-byte chunk per store; otherwise half a chunk at
+        // a time, to bound the registers held next to the accumulators.
         half_t* __restrict__ qk = which == 0 ? pa.Q : pa.K;
         const float oscale = which == 0 ? pa.qscale : 1.f;  // Q leaves pre-scaled, one rounding
         half_t* dst = qk + (static_cast<int64_t>(b * H) * (d / 8) + c0 / 8) * L * 8 + static_cast<int64_t>(t) * P * 8;
-        if constexpr (MB == 1) {
+        if constexpr (MB == 1 && H == 16) {
           half8 stg[16];
 #pragma unroll
           for (int cl = 0; cl < 8; ++cl) {
-            const floatx16 o = mix_block<MB>(acc[cl >> 1][j], cl & 1, ah[0], alo[0]);
+            const floatx16 o = mixc(j, cl, 0);
 #pragma unroll
             for (int r = 0; r < 16; ++r) stg[r][cl] = static_cast<half_t>(o[r] * oscale);
           }
@@ -310,8 +408,7 @@ __global__ __launch_bounds__(GThreads, 1) void gemm_mix_bf16_kernel(NtArgs g, Pr
               half4 stg[16];
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
-                const int cl = 4 * half + q;
-                const floatx16 o = mix_block<MB>(acc[cl >> 1][j], cl & 1, ah[mb], alo[mb]);
+                const floatx16 o = mixc(j, 4 * half + q, mb);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) stg[r][q] = static_cast<half_t>(o[r] * oscale);
               }
@@ -331,7 +428,7 @@ __global__ __launch_bounds__(GThreads, 1) void gemm_mix_bf16_kernel(NtArgs g, Pr
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int cl = 0; cl < 8; ++cl) {
-            const floatx16 o = mix_block<MB>(acc[cl >> 1][j], cl & 1, ah[mb], alo[mb]);
+            const floatx16 o = mixc(j, cl, mb);
             const int c = c0 + cl;
             half_t* dst = pa.Vt + (static_cast<int64_t>(b * H) * d + c) * L + static_cast<int64_t>(t) * P;
 #pragma unroll
@@ -691,22 +788,18 @@ void launch_mix(const ProjArgs& pa, hipStream_t s) {
 // fp32 first rows of the fused path: the mixing of the unmixed fp32 projections Ye of each
 // sequence's first T0 tokens (fp32 FMAs).  One thread per (b, t, which, h, c); grid
 // (D / 256, B * T0 * 3).  The H = 16 source values and coefficients are all loaded up front.
+template <int H>
 __global__ __launch_bounds__(256) void early_mix_kernel(ProjArgs pa) {
-  constexpr int H = kFusedH;
   const int d = pa.d, D = pa.D, P = pa.P, R = pa.R, T0 = pa.T0;
   const int hc = blockIdx.x * 256 + threadIdx.x;
   const int which = blockIdx.y % 3, bt = blockIdx.y / 3;
   const int t = bt % T0, b = bt / T0;
   const int h = hc / d, c = hc % d;
-  const float* __restrict__ y = pa.Ye + static_cast<int64_t>(bt) * 3 * D + which * D + c * H;
+  const float* __restrict__ y = pa.Ye + static_cast<int64_t>(bt) * 3 * D + which * D;
   const float* __restrict__ al = pa.alpha[which];
   float ym[H];
 #pragma unroll
-  for (int q = 0; q < H / 4; ++q) {
-    const floatx4 v = *reinterpret_cast<const floatx4*>(y + 4 * q);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ym[4 * q + e] = v[e];
-  }
+  for (int m = 0; m < H; ++m) ym[m] = y[fused_row(c, m, H)];
   for (int j = 0; j < P; ++j) {
     const int i = t * P + j;
     if (i >= R) break;
@@ -737,20 +830,26 @@ hipError_t launch_proj_bf16(const ProjArgs& pa, hipStream_t s, hipEvent_t ev_pre
     g.I = 3 * D;
     g.J = M;
     g.K = D;
-    const int64_t tiles = static_cast<int64_t>(3 * D / GTI) * ((M + GTJ - 1) / GTJ);
+    const int ti = pa.H == 20 ? 320 : 256;
+    const int64_t tiles = static_cast<int64_t>(3 * D / ti) * ((M + GTJ - 1) / GTJ);
     if (static_cast<int64_t>(M) * D * 2 >= (int64_t{1} << 31) || static_cast<int64_t>(3) * D * D * 2 >= (int64_t{1} << 31))
       return hipErrorInvalidValue;
-    switch (pa.P) {
-      case 1: hipLaunchKernelGGL((gemm_mix_bf16_kernel<1>), dim3(tiles), dim3(GThreads), 0, s, g, pa); break;
-      case 2: hipLaunchKernelGGL((gemm_mix_bf16_kernel<2>), dim3(tiles), dim3(GThreads), 0, s, g, pa); break;
-      default: hipLaunchKernelGGL((gemm_mix_bf16_kernel<4>), dim3(tiles), dim3(GThreads), 0, s, g, pa); break;
+    const int key = pa.H * 8 + pa.P;
+    switch (key) {
+      case 16 * 8 + 1: hipLaunchKernelGGL((gemm_mix_bf16_kernel<16, 1>), dim3(tiles), dim3(GThreads), 0, s, g, pa); break;
+      case 16 * 8 + 2: hipLaunchKernelGGL((gemm_mix_bf16_kernel<16, 2>), dim3(tiles), dim3(GThreads), 0, s, g, pa); break;
+      case 20 * 8 + 1: hipLaunchKernelGGL((gemm_mix_bf16_kernel<20, 1>), dim3(tiles), dim3(GThreads), 0, s, g, pa); break;
+      case 20 * 8 + 2: hipLaunchKernelGGL((gemm_mix_bf16_kernel<20, 2>), dim3(tiles), dim3(GThreads), 0, s, g, pa); break;
+      default: return hipErrorInvalidValue;
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // the mixing is part of the GEMM; what is left of the mixing step is the fp32 mixing
     // of the first tokens
     if (ev_gemm && (e = hipEventRecord(ev_gemm, s)) != hipSuccess) return e;
     if (pa.R > 0) {
-      hipLaunchKernelGGL(early_mix_kernel, dim3(D / 256, pa.B * pa.T0 * 3), dim3(256), 0, s, pa);
+      const dim3 eg(D / 256, pa.B * pa.T0 * 3);
+      if (pa.H == 20) hipLaunchKernelGGL(early_mix_kernel<20>, eg, dim3(256), 0, s, pa);
+      else hipLaunchKernelGGL(early_mix_kernel<16>, eg, dim3(256), 0, s, pa);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;

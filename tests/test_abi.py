@@ -55,15 +55,19 @@ def test_workspace_size_covers_the_intermediates():
 
 @pytest.mark.parametrize("B,N,D,H,P,dtype,fused", [
     (4, 4096, 2048, 16, 2, bd.IHA_BF16, True),     # 16 heads of 128, P in {1, 2, 4}
-    (2, 256, 1024, 16, 4, bd.IHA_BF16, True),
+    (2, 256, 1024, 16, 4, bd.IHA_BF16, False),     # P = 4 keeps GEMM + separate mixing
     (2, 256, 1024, 16, 1, bd.IHA_BF16, True),
     (2, 256, 1024, 16, 3, bd.IHA_BF16, False),     # P = 3
-    (2, 8192, 2560, 20, 4, bd.IHA_BF16, False),    # H = 20
+    (2, 8192, 2560, 20, 4, bd.IHA_BF16, False),    # P = 4
+    (2, 8192, 2560, 20, 2, bd.IHA_BF16, True),     # 20 heads, D a multiple of 320
+    (2, 256, 1280, 20, 2, bd.IHA_BF16, True),
+    (2, 256, 640, 5, 2, bd.IHA_BF16, False),       # H = 5
     (2, 256, 1024, 16, 2, bd.IHA_F32, False),      # fp32 folds the mixing into the weights
 ])
 def test_plan_and_workspace_follow_the_fused_mixing(B, N, D, H, P, dtype, fused):
-    """IHA_PLAN_MIX_FUSED is set exactly for bf16 with 16 heads, D a multiple of 256 and
-    P in {1, 2, 4}; then the workspace holds no fp32 projections of all tokens."""
+    """IHA_PLAN_MIX_FUSED is set exactly for bf16 with 16 heads and D a multiple of 256, or 20
+    heads and D a multiple of 320, and P in {1, 2}; then the workspace holds no fp32
+    projections of all tokens."""
     p = bd.make_problem(B, N, D, H, P, "causal", None, dtype)
     assert bd.iha_plan(p) == (bd.IHA_PLAN_MIX_FUSED if fused else 0)
     n = bd.iha_workspace_bytes(p)

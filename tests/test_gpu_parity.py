@@ -94,8 +94,13 @@ SMALL = [
     (1, 256, 256, 2, 2, "causal", None, "bf16"),     # H = 2
     (2, 128, 320, 5, 4, "window", 37, "bf16"),       # H = 5 (odd), P = 4, d = 64
     (1, 128, 192, 3, 1, "none", None, "bf16"),       # H = 3, P = 1: heads past H skipped
-    (1, 384, 2560, 20, 4, "window", 100, "bf16"),    # H = 20: two k-steps, three row blocks
+    (1, 384, 2560, 20, 4, "window", 100, "bf16"),    # H = 20, P = 4: GEMM + separate mixing
     (2, 128, 1024, 16, 2, "causal", None, "bf16"),   # H = 16, P = 2
+    # the fused projection + mixing with 20 heads (320-row tiles, heads 16..19 in a rest block)
+    (1, 200, 1280, 20, 1, "causal", None, "bf16"),   # d = 64, P = 1, ragged token tile
+    (2, 100, 2560, 20, 2, "window", 33, "bf16"),     # P = 2, two sequences in one token tile
+    (1, 130, 1280, 20, 2, "none", None, "bf16"),     # no first-row recomputation
+    (1, 128, 1024, 16, 1, "window", 21, "bf16"),     # H = 16, P = 1 fused
 ]
 
 
