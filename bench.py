@@ -18,7 +18,8 @@ Work per unit (algorithmic, the count the pages' convention gives):
              epilogue (IHA_PLAN_MIX_FUSED) the gemm step holds it and the mix step is the
              fp32 mixing of the first tokens only: 3 * D * 4 read per first token and
              3 * D * 4 written per first stacked row
-  collapse   bytes: P*H*d*4 read + H*d*4 written per token
+  collapse   bytes: P*H*d*e read (e = 2: the bf16 forward keeps the stacked outputs in fp16;
+             4 for fp32) + H*d*4 written per token
   prep       bytes: 3*D^2*2 read + 3*D^2*2 written (bf16 weight transpose)
 """
 import argparse
@@ -139,8 +140,8 @@ def run_workload(w, steps, warmup):
              "gemm": roof("mfma", 6.0 * B * N * D * D, kms["gemm"]),
              "mix": mix,
              "attention": roof("mfma", attn_flops, kms["attention"]),
-             "collapse": roof("hbm", B * N * (P * H * d * 4 + H * d * 4) + H * H * P * 4,
-                              kms["collapse"])}
+             "collapse": roof("hbm", B * N * (P * H * d * (2 if w.dtype == "bf16" else 4) + H * d * 4)
+                              + H * H * P * 4, kms["collapse"])}
     roofs = {k: v for k, v in roofs.items() if v is not None}
     return x, {"ms_step": ms_step, "value": B * P * N / (ms_step * 1e-3), "kms": kms,
                "roofs": roofs, "mix_fused": fused}

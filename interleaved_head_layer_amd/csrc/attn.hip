@@ -293,6 +293,7 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
   const int qt = (MASK == kMaskCausal) ? (nqt - 1 - qi) : qi;
   const int b = bh / H, h = bh % H;
   const int q0 = qt * ABM;
+  if (a.skip_first && qt == 0) return;  // rows recomputed elsewhere (whole workgroup)
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
   const half_t* __restrict__ Qb = static_cast<const half_t*>(a.Q) + qbase;
   const half_t* __restrict__ Kb = static_cast<const half_t*>(a.K) + qbase;
   const half_t* __restrict__ Vb = static_cast<const half_t*>(a.Vt) + static_cast<int64_t>(b * H + h) * DH * L;
-  float* __restrict__ Ob = a.O + static_cast<int64_t>(b) * L * rs + h * DH;
+  const int64_t obase = static_cast<int64_t>(b) * L * rs + h * DH;
 
   // Q fragments: all loads in flight at once (rows past the end read the last row, whose
   // results are never stored), then the first K/V tile, then the optional scale.
@@ -385,16 +386,28 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
       inv = 0.f;
       if (a.flag) atomicOr(a.flag, kFlagEmptyRow);
     }
-    float* orow = Ob + qrow * rs;
+    const int64_t orow = obase + static_cast<int64_t>(qrow) * rs;
+    if (a.Oh) {  // fp16 output
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
+      for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        floatx4 v;
+        for (int q = 0; q < 4; ++q) {
+          half4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = st.o[cb][4 * q + e] * inv;
-        *reinterpret_cast<floatx4*>(orow + cb * 32 + 8 * q + 4 * hf) = v;
-      }
+          for (int e = 0; e < 4; ++e) v[e] = static_cast<half_t>(st.o[cb][4 * q + e] * inv);
+          *reinterpret_cast<half4*>(a.Oh + orow + cb * 32 + 8 * q + 4 * hf) = v;
+        }
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          floatx4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = st.o[cb][4 * q + e] * inv;
+          *reinterpret_cast<floatx4*>(a.O + orow + cb * 32 + 8 * q + 4 * hf) = v;
+        }
+    }
   }
 }
 

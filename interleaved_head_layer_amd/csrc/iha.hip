@@ -22,7 +22,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
 struct Layout {
-  size_t flag, wt, yqk, yvt, ye, q, k, vt, pbar, qe, ke, vte, total;
+  size_t flag, wt, yqk, yvt, ye, q, k, vt, pbar, pe, qe, ke, vte, total;
   int R;  // precise first stacked rows (0 when unused)
 };
 
@@ -80,14 +80,16 @@ Layout layout_of(const iha_problem& p) {
   L.q = take(act * e);
   L.k = take(act * e);
   L.vt = take(act * e);
-  L.pbar = take(act * 4);
-  // bf16 inputs under a causal or window mask: fp32 copies of the first rows.
+  L.pbar = take(act * e);  // stacked attention outputs: fp16 (bf16 inputs) or fp32
+  // bf16 inputs under a causal or window mask: fp32 copies of the first rows' queries, keys
+  // and values, and their fp32 attention outputs.
   if (p.dtype == IHA_BF16 && p.mask != IHA_MASK_NONE) {
     const int64_t R = std::min<int64_t>(iha::kPreciseRows, p.P * p.N);
     L.R = static_cast<int>(R);
     L.qe = take(static_cast<size_t>(p.B) * R * p.D * 4);
     L.ke = take(static_cast<size_t>(p.B) * R * p.D * 4);
     L.vte = take(static_cast<size_t>(p.B) * R * p.D * 4);
+    L.pe = take(static_cast<size_t>(p.B) * R * p.D * 4);
     if (iha::fused_shape(p.H, p.D, p.P))  // unmixed projections of the first tokens
       L.ye = take(static_cast<size_t>(p.B) * ((R + p.P - 1) / p.P) * 3 * p.D * 4);
   }
@@ -229,7 +231,6 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
   at.Q = ws + lay.q;
   at.K = ws + lay.k;
   at.Vt = ws + lay.vt;
-  at.O = reinterpret_cast<float*>(ws + lay.pbar);
   at.flag = flag;
   at.B = B;
   at.L = P * N;
@@ -241,11 +242,15 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
                   : 0;
   const float score_scale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
   at.qk_scale = score_scale;
+  static_assert(iha::kPreciseRows == 128, "the fp32 first rows are the fp16 kernel's query tile 0");
   if (bf16) {
     at.qk_scale = 1.f;  // the fp16 Q was stored pre-scaled
     at.qk_layout = qk_layout;
+    at.Oh = reinterpret_cast<iha::half_t*>(ws + lay.pbar);  // fp16 stacked outputs
+    at.skip_first = lay.R > 0;  // rows 0 .. R-1 (query tile 0) come from the fp32 recomputation
     IHA_HIP(iha::launch_attn_f16(at, stream));
   } else {
+    at.O = reinterpret_cast<float*>(ws + lay.pbar);
     IHA_HIP(iha::launch_attn_f32(at, stream));
   }
   if (ev) IHA_HIP(hipEventRecord(ev[4], stream));
@@ -260,13 +265,17 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
     ea.D = D;
     ea.d = d;
     ea.R = lay.R;
-    IHA_HIP(iha::launch_early_attn(ea, at.O, static_cast<int64_t>(at.L) * H * d, p.mask,
-                                   std::min(at.window, lay.R), score_scale, stream));
+    IHA_HIP(iha::launch_early_attn(ea, reinterpret_cast<float*>(ws + lay.pe), static_cast<int64_t>(lay.R) * H * d,
+                                   p.mask, std::min(at.window, lay.R), score_scale, stream));
   }
   if (ev) IHA_HIP(hipEventRecord(ev[5], stream));
 
   // Steps 4-5: unstack, collapse with R, concatenate heads.
-  IHA_HIP(iha::launch_collapse(at.O, R, X_out, B * N, H, P, d, stream));
+  if (bf16)
+    IHA_HIP(iha::launch_collapse_h(at.Oh, lay.R > 0 ? reinterpret_cast<const float*>(ws + lay.pe) : nullptr, lay.R, R,
+                                   X_out, B, N, H, P, d, stream));
+  else
+    IHA_HIP(iha::launch_collapse(at.O, R, X_out, B * N, H, P, d, stream));
   if (ev) IHA_HIP(hipEventRecord(ev[6], stream));
 
   if (p.flags & IHA_FLAG_CHECK) {

@@ -42,7 +42,9 @@ struct AttnArgs {
   const void* Q;   // [B][L][H][d] or chunked (qk_layout; fp16 kernel only)
   const void* K;   // same layout as Q
   const void* Vt;  // [B][H][d][L]
-  float* O;        // [B][L][H][d]
+  float* O;        // [B][L][H][d] fp32, or null with Oh
+  half_t* Oh;      // fp16 kernel only: [B][L][H][d] fp16 output instead of O (may be null)
+  int skip_first;  // fp16 kernel only: query tile 0 (rows 0..127) is not computed
   unsigned* flag;  // may be null
   int B, L, H, d, mask, window;
   float qk_scale;     // multiplies q . k to give base-2 scores
@@ -109,6 +111,10 @@ constexpr int kPreciseRows = 128;
 
 // Unstack + collapse + concatenation:
 //   out[tok][h*d + c] = sum_{h', j} R[h][h'*P + j] * Pbar[tok*P + j][h'][c]
+// Collapse from fp16 stacked outputs Ph [B*N*P][H][d] whose first R stacked rows of every
+// sequence come instead from the fp32 rows Pe [B][R][H][d].
+hipError_t launch_collapse_h(const half_t* Ph, const float* Pe, int R, const float* Rm, float* out, int B,
+                             int N, int H, int P, int d, hipStream_t s);
 hipError_t launch_collapse(const float* Pbar, const float* R, float* out, int ntok, int H, int P,
                            int d, hipStream_t s);
 

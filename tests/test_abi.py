@@ -45,12 +45,12 @@ def test_workspace_size_covers_the_intermediates():
     B, N, D, P = 2, 100, 256, 2
     M, rows = B * N, B * N * P
     need = 3 * D * D * 2 + M * 2 * D * 4 + M * D * 4      # transposed W, fp32 projections
-    need += 3 * rows * D * 2 + rows * D * 4                # Q~, K~, V~^T (fp16), P-bar (fp32)
-    R = min(128, P * N)                                    # fp32 first rows (bf16, masked)
-    need += 3 * B * R * D * 4
+    need += 4 * rows * D * 2                               # Q~, K~, V~^T, P-bar (fp16)
+    R = min(128, P * N)                                    # fp32 first rows (bf16, masked):
+    need += 4 * B * R * D * 4                              # their q, k, v and outputs
     assert need <= n <= need + 16 * 256
     st, n_none = _ws(mask="none")
-    assert st == bd.IHA_OK and n_none < need - 3 * B * R * D * 4 + 16 * 256
+    assert st == bd.IHA_OK and n_none < need - 4 * B * R * D * 4 + 16 * 256
 
 
 @pytest.mark.parametrize("B,N,D,H,P,dtype,fused", [
@@ -71,12 +71,12 @@ def test_plan_and_workspace_follow_the_fused_mixing(B, N, D, H, P, dtype, fused)
     p = bd.make_problem(B, N, D, H, P, "causal", None, dtype)
     assert bd.iha_plan(p) == (bd.IHA_PLAN_MIX_FUSED if fused else 0)
     n = bd.iha_workspace_bytes(p)
-    stacked = 3 * B * P * N * D * 2 + B * P * N * D * 4           # Q~ K~ V~^T, P-bar
+    stacked = 4 * B * P * N * D * 2                               # Q~ K~ V~^T, P-bar (fp16)
     if dtype == bd.IHA_BF16:
         stacked += 3 * D * D * 2                                  # transposed weights
     if dtype == bd.IHA_BF16:                                      # fp32 first rows (causal)
         R = min(128, P * N)
-        stacked += 3 * B * R * D * 4
+        stacked += 4 * B * R * D * 4                              # their q, k, v, outputs
         if fused:
             stacked += B * -(-R // P) * 3 * D * 4                 # their unmixed projections
     fp32_proj = B * N * 3 * D * 4
