@@ -655,54 +655,53 @@ __device__ __forceinline__ void alpha_operands(const float* __restrict__ al, int
       }
 }
 
-// V~^T from Y_V^T.  A wave owns one channel c and 128 tokens of one sequence: lane n (of 32)
-// loads float4s of tokens 4n..4n+3, so column n of product block q is token 4n + q; after the
-// four blocks a lane holds, for each of its (h, j) rows, four consecutive tokens, i.e. 4*P
-// consecutive fp16 of V~^T[b][h][c][*] (P in {1, 2, 4}).  grid (ceil(M / 512), d), 256 threads.
-template <int P, int MB, int KS>
+// V~^T from Y_V^T.  A wave owns one channel c and 32*TQ tokens of one sequence: lane n (of
+// 32) loads TQ consecutive tokens TQ*n .. TQ*n + TQ-1, so column n of product block q is
+// token TQ*n + q; after the TQ blocks a lane holds, for each of its (h, j) rows, TQ
+// consecutive tokens, i.e. TQ*P consecutive fp16 of V~^T[b][h][c][*] (P in {1, 2, 4}).
+// TQ = 2 halves the registers of the large cases (more waves in flight).  grid
+// (ceil(M / (128 TQ)), d), 256 threads.
+template <int P, int MB, int KS, int TQ>
 __global__ __launch_bounds__(256) void mix_v_mfma_kernel(ProjArgs pa) {
+  typedef float floatq __attribute__((ext_vector_type(TQ)));
   const int M = pa.B * pa.N, d = pa.d, H = pa.H, N = pa.N;
   const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
-  // The four waves take consecutive 128-token blocks of one channel: 2 KB runs per row.
+  // The four waves take consecutive blocks of one channel: 128*TQ*4 bytes runs per row.
   const int c = blockIdx.y;
-  const int tok0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 128;  // N % 128 == 0: one sequence
+  const int tok0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 32 * TQ;  // N % 128 == 0: one sequence
   if (tok0 >= M) return;
   const int b = tok0 / N, t0 = tok0 % N;
-  // B operands, blocks q = 0..3: B[k][n] = Y_V^T[m = ks*16 + 8*hf + k%8][token 4n + q].
-  half8 bh[4][KS], bl[4][KS];
-  floatx4 yall[KS][8];
+  // B operands, blocks q < TQ: B[k][n] = Y_V^T[m = ks*16 + 8*hf + k%8][token TQ*n + q].
+  half8 bh[TQ][KS], bl[TQ][KS];
+  floatq yall[KS][8];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int m = ks * 16 + 8 * hf + e;
-      yall[ks][e] = *reinterpret_cast<const floatx4*>(pa.Yvt + static_cast<int64_t>((m < H ? m : 0) * d + c) * M + tok0 + 4 * n);
+      yall[ks][e] = *reinterpret_cast<const floatq*>(pa.Yvt + static_cast<int64_t>((m < H ? m : 0) * d + c) * M + tok0 + TQ * n);
     }
   half8 ah[MB][KS], alo[MB][KS];
   alpha_operands<MB, KS>(pa.alpha[2], H, P, ah, alo);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    floatx4 y[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int m = ks * 16 + 8 * hf + e;
-      y[e] = m < H ? yall[ks][e] : floatx4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < TQ; ++q)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        bh[q][ks][e] = hi_f16(y[e][q]);
-        bl[q][ks][e] = lo_f16(y[e][q]);
+        const int m = ks * 16 + 8 * hf + e;
+        const float y = m < H ? yall[ks][e][q] : 0.f;
+        bh[q][ks][e] = hi_f16(y);
+        bl[q][ks][e] = lo_f16(y);
       }
   }
   const int64_t L = static_cast<int64_t>(P) * N;
   const int HP = H * P;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    floatx16 acc[4];
+    floatx16 acc[TQ];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < TQ; ++q) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[q][r] = 0.f;
 #pragma unroll
@@ -721,22 +720,22 @@ __global__ __launch_bounds__(256) void mix_v_mfma_kernel(ProjArgs pa) {
       for (int u = 0; u < 4 / P; ++u) {  // heads among these 4 rows
         const int h = (row0 + u * P) / P;
         if (h >= H) continue;
-        // 4 tokens x P pseudo-tokens of head h, stacked positions (t0 + 4n + q)*P + j
-        typedef _Float16 halfv __attribute__((ext_vector_type(4 * P)));
+        // TQ tokens x P pseudo-tokens of head h, stacked positions (t0 + TQ*n + q)*P + j
+        typedef _Float16 halfv __attribute__((ext_vector_type(TQ * P)));
         halfv v;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < TQ; ++q)
 #pragma unroll
           for (int j = 0; j < P; ++j) v[q * P + j] = static_cast<half_t>(acc[q][4 * g + u * P + j]);
-        half_t* dst = pa.Vt + (static_cast<int64_t>(b * H + h) * d + c) * L + static_cast<int64_t>(t0 + 4 * n) * P;
+        half_t* dst = pa.Vt + (static_cast<int64_t>(b * H + h) * d + c) * L + static_cast<int64_t>(t0 + TQ * n) * P;
         *reinterpret_cast<halfv*>(dst) = v;
-        if (pa.Vte && (t0 + 4 * n) * P < pa.R) {
+        if (pa.Vte && (t0 + TQ * n) * P < pa.R) {
           float* erow = pa.Vte + (static_cast<int64_t>(b * H + h) * d + c) * pa.R;
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
+          for (int q = 0; q < TQ; ++q)
 #pragma unroll
             for (int j = 0; j < P; ++j) {
-              const int i = (t0 + 4 * n + q) * P + j;
+              const int i = (t0 + TQ * n + q) * P + j;
               if (i < pa.R) erow[i] = acc[q][4 * g + u * P + j];
             }
         }
@@ -748,18 +747,16 @@ __global__ __launch_bounds__(256) void mix_v_mfma_kernel(ProjArgs pa) {
 template <int P>
 bool launch_mix_v_mfma_p(const ProjArgs& pa, hipStream_t s) {
   const int M = pa.B * pa.N;
-  const dim3 grid((M + 511) / 512, pa.d);
   const int mb = (pa.H * P + 31) / 32, ks = (pa.H + 15) / 16;
-  if (mb == 1 && ks == 1) hipLaunchKernelGGL((mix_v_mfma_kernel<P, 1, 1>), grid, dim3(256), 0, s, pa);
-  else if (mb <= 2 && ks == 1) hipLaunchKernelGGL((mix_v_mfma_kernel<P, 2, 1>), grid, dim3(256), 0, s, pa);
-  else if (mb <= 3 && ks <= 2) hipLaunchKernelGGL((mix_v_mfma_kernel<P, 3, 2>), grid, dim3(256), 0, s, pa);
-  else if (mb <= 4 && ks <= 2) hipLaunchKernelGGL((mix_v_mfma_kernel<P, 4, 2>), grid, dim3(256), 0, s, pa);
+  const dim3 g4((M + 511) / 512, pa.d), g2((M + 255) / 256, pa.d);
+  if (mb == 1 && ks == 1) hipLaunchKernelGGL((mix_v_mfma_kernel<P, 1, 1, 4>), g4, dim3(256), 0, s, pa);
+  else if (mb <= 2 && ks == 1) hipLaunchKernelGGL((mix_v_mfma_kernel<P, 2, 1, 4>), g4, dim3(256), 0, s, pa);
+  else if (mb <= 3 && ks <= 2) hipLaunchKernelGGL((mix_v_mfma_kernel<P, 3, 2, 2>), g2, dim3(256), 0, s, pa);
+  else if (mb <= 4 && ks <= 2) hipLaunchKernelGGL((mix_v_mfma_kernel<P, 4, 2, 2>), g2, dim3(256), 0, s, pa);
   else return false;
   return true;
 }
 
-// The matrix-core V mixing: P in {1, 2, 4}, whole 128-token blocks per sequence,
-// H*P <= 128 and H <= 32.  Returns false (nothing launched) otherwise.
 bool launch_mix_v_mfma(const ProjArgs& pa, hipStream_t s) {
   if (pa.N % 128 != 0 || pa.H > 32 || pa.H * pa.P > 128) return false;
   switch (pa.P) {
