@@ -207,7 +207,7 @@ def main():
 
     extra = {}
     if not args.no_extra:
-        for name in wl.HEADLINE:
+        for name in wl.HEADLINE + ["mha_causal_bf16"]:   # + the P = 1 MHA configuration
             if name == w.name:
                 continue
             _, e = run_workload(wl.WORKLOADS[name], args.extra_steps, 2)
