@@ -101,6 +101,8 @@ SMALL = [
     (2, 100, 2560, 20, 2, "window", 33, "bf16"),     # P = 2, two sequences in one token tile
     (1, 130, 1280, 20, 2, "none", None, "bf16"),     # no first-row recomputation
     (1, 128, 1024, 16, 1, "window", 21, "bf16"),     # H = 16, P = 1 fused
+    (2, 256, 256, 4, 2, "window", None, "bf16"),     # W_s = 64: one key tile per query tile
+    (4, 512, 512, 4, 2, "window", 300, "bf16"),      # window edges inside key tiles
 ]
 
 
