@@ -41,7 +41,7 @@ __global__ __launch_bounds__(EThreads) void early_attn_kernel(EarlyArgs e, float
   const int r = tid / EGroup, g = tid % EGroup;
   const float* __restrict__ Qb = e.Qe + static_cast<int64_t>(b) * R * D + h * DH;
   const float* __restrict__ Kb = e.Ke + static_cast<int64_t>(b) * R * D + h * DH;
-  const float* __restrict__ Vb = e.Vte + static_cast<int64_t>(b * H + h) * DH * R;
+  const float* __restrict__ Vb = e.Ve + static_cast<int64_t>(b) * R * D + h * DH;
 
   const int khi = min(R, i0 + ERows);  // keys <= the block's last row
   const int klo = mask == kMaskWindow ? max(0, i0 - window + 1) : 0;
@@ -67,15 +67,15 @@ __global__ __launch_bounds__(EThreads) void early_attn_kernel(EarlyArgs e, float
     kreg[q] = floatx4{0.f, 0.f, 0.f, 0.f};
     if (n < nk) kreg[q] = *reinterpret_cast<const floatx4*>(Kb + static_cast<int64_t>(kc0 + n) * D + c);
   }
-  // Values V^T[c][kc0 + n] for n < nk4 into registers (rows of V^T have stride R, which need
-  // not be a multiple of 4, so these are scalar loads).
-  constexpr int VPT = DH * kPreciseRows / EThreads;
-  float vreg[VPT];
+  // Values V[kc0 + n][c] for n < nk4 into registers as float4 over c (zero past nk); they
+  // go to LDS transposed (V^T[c][n]) once the scores are done.
+  constexpr int VPT = KPT;
+  floatx4 vreg[VPT];
 #pragma unroll
   for (int q = 0; q < VPT; ++q) {
-    const int x = tid + q * EThreads;
-    const int c = x / kPreciseRows, n = x % kPreciseRows;
-    vreg[q] = (n < nk) ? Vb[static_cast<int64_t>(c) * R + kc0 + n] : 0.f;
+    const int x = tid + q * EThreads, n = x / C4, c = (x % C4) * 4;
+    vreg[q] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (n < nk) vreg[q] = *reinterpret_cast<const floatx4*>(Vb + static_cast<int64_t>(kc0 + n) * D + c);
   }
 #pragma unroll
   for (int q = 0; q < QPT; ++q) {
@@ -135,7 +135,9 @@ __global__ __launch_bounds__(EThreads) void early_attn_kernel(EarlyArgs e, float
 #pragma unroll
   for (int q = 0; q < VPT; ++q) {
     const int x = tid + q * EThreads;
-    kv[x / kPreciseRows][x % kPreciseRows] = vreg[q];
+    const int n = x / C4, c = (x % C4) * 4;
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) kv[c + e4][n] = vreg[q][e4];
   }
   __syncthreads();
 

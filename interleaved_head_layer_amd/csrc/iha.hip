@@ -174,7 +174,7 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
     if (lay.R > 0) {
       pa.Qe = reinterpret_cast<float*>(ws + lay.qe);
       pa.Ke = reinterpret_cast<float*>(ws + lay.ke);
-      pa.Vte = reinterpret_cast<float*>(ws + lay.vte);
+      pa.Ve = reinterpret_cast<float*>(ws + lay.vte);
       pa.Ye = reinterpret_cast<float*>(ws + lay.ye);
     }
     pa.B = B;
@@ -186,7 +186,7 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
     pa.R = lay.R;
     pa.T0 = (lay.R + P - 1) / P;
     pa.qscale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
-    IHA_HIP(iha::launch_clear_flag(flag, stream));
+    pa.flag = flag;  // cleared by the weight transpose
     if (iha::proj_fused(pa)) qk_layout = iha::kQKChunked;
     IHA_HIP(iha::launch_proj_bf16(pa, stream, ev ? ev[1] : nullptr, ev ? ev[2] : nullptr));
   } else {
@@ -259,7 +259,7 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
     iha::EarlyArgs ea{};
     ea.Qe = reinterpret_cast<float*>(ws + lay.qe);
     ea.Ke = reinterpret_cast<float*>(ws + lay.ke);
-    ea.Vte = reinterpret_cast<float*>(ws + lay.vte);
+    ea.Ve = reinterpret_cast<float*>(ws + lay.vte);
     ea.B = B;
     ea.H = H;
     ea.D = D;

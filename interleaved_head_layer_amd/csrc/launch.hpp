@@ -74,11 +74,12 @@ struct ProjArgs {
   half_t* Vt;             // [B][H][d][P*N] fp16
   float* Qe;              // fp32 copies of the first R stacked rows (or null)
   float* Ke;
-  float* Vte;
+  float* Ve;
   float* Ye;              // fused path: [B][T0][3D] unmixed fp32 projections of the first tokens
   int B, N, D, H, d, P, R;
   int T0;                 // ceil(R / P): tokens whose pseudo-tokens include a first row
   float qscale;           // factor applied to the fp16 Q (the base-2 score scale)
+  unsigned* flag;         // status word, cleared by the first kernel (may be null)
 };
 // With P = 4 the fused epilogue writes four stacked outputs per projected value and its
 // stores no longer hide behind the products (measured: slower than GEMM + mixing), so the
@@ -96,11 +97,11 @@ bool proj_fused(const ProjArgs& pa);
 hipError_t launch_proj_bf16(const ProjArgs& pa, hipStream_t s, hipEvent_t ev_prep, hipEvent_t ev_gemm);
 
 // fp32 copies of the first R stacked rows (R = min(128, P*N)) of every (b, h) for bf16
-// inputs under a causal or window mask: Qe, Ke [B][R][H][d], Vte [B][H][d][R].
+// inputs under a causal or window mask: Qe, Ke, Ve [B][R][H][d].
 struct EarlyArgs {
   const float* Qe;
   const float* Ke;
-  const float* Vte;
+  const float* Ve;
   int B, H, D, d, R;
 };
 // fp32 attention of those rows (causal / window), written into O rows < R

@@ -9,7 +9,7 @@
 //           Y_V^T [D][M]  = Wt_V X^T      (channel-major)  fp32
 //   mix_qk  Q~, K~ [B][P*N][H][d] fp16, rows t*P + j
 //   mix_v   V~^T  [B][H][d][P*N]  fp16
-// The first T0 tokens of every sequence also get fp32 copies (Qe, Ke, Vte) for the
+// The first T0 tokens of every sequence also get fp32 copies (Qe, Ke, Ve) for the
 // full-precision first rows.
 #include "common.hpp"
 #include "launch.hpp"
@@ -38,6 +38,8 @@ __global__ __launch_bounds__(256) void wprep_kernel(ProjArgs pa, int cm) {
   const int D = pa.D, d = pa.d, H = pa.H;
   const int k0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
   const int tid = threadIdx.x;
+  // The forward's status word starts at zero: this is its first kernel.
+  if (pa.flag && (blockIdx.x | blockIdx.y | blockIdx.z | tid) == 0) *pa.flag = 0u;
 #pragma unroll
   for (int q = 0; q < 2; ++q) {  // 64 rows of 8 x 16 bytes
     const int x = tid + 256 * q, r = x >> 3, c8 = (x & 7) * 8;
@@ -587,10 +589,10 @@ __global__ __launch_bounds__(256) void mix_v_kernel(ProjArgs pa) {
           const int i = (t0 + w) * P + j;
           const half2v v = {static_cast<half_t>(a0[w]), static_cast<half_t>(a1[w])};
           *reinterpret_cast<half2v*>(vrow + i) = v;
-          if (pa.Vte && i < pa.R) {
-            float* erow = pa.Vte + (static_cast<int64_t>(b0 * H + h) * d + c) * pa.R;
-            erow[i] = a0[w];
-            if (i + 1 < pa.R) erow[i + 1] = a1[w];
+          if (pa.Ve && i < pa.R) {
+            float* erow = pa.Ve + static_cast<int64_t>(b0) * pa.R * pa.D + h * d + c;
+            erow[static_cast<int64_t>(i) * pa.D] = a0[w];
+            if (i + 1 < pa.R) erow[static_cast<int64_t>(i + 1) * pa.D] = a1[w];
           }
         }
       }
@@ -607,7 +609,7 @@ __global__ __launch_bounds__(256) void mix_v_kernel(ProjArgs pa) {
         half_t* __restrict__ vrow = pa.Vt + (static_cast<int64_t>(b * H + h) * d + c) * L;
         vrow[static_cast<int64_t>(t) * P + j] = static_cast<half_t>(acc[w]);
         const int i = t * P + j;
-        if (pa.Vte && i < pa.R) pa.Vte[(static_cast<int64_t>(b * H + h) * d + c) * pa.R + i] = acc[w];
+        if (pa.Ve && i < pa.R) pa.Ve[(static_cast<int64_t>(b) * pa.R + i) * pa.D + h * d + c] = acc[w];
       }
     }
   }
@@ -729,14 +731,14 @@ __global__ __launch_bounds__(256) void mix_v_mfma_kernel(ProjArgs pa) {
           for (int j = 0; j < P; ++j) v[q * P + j] = static_cast<half_t>(acc[q][4 * g + u * P + j]);
         half_t* dst = pa.Vt + (static_cast<int64_t>(b * H + h) * d + c) * L + static_cast<int64_t>(t0 + TQ * n) * P;
         *reinterpret_cast<halfv*>(dst) = v;
-        if (pa.Vte && (t0 + TQ * n) * P < pa.R) {
-          float* erow = pa.Vte + (static_cast<int64_t>(b * H + h) * d + c) * pa.R;
+        if (pa.Ve && (t0 + TQ * n) * P < pa.R) {
+          float* erow = pa.Ve + static_cast<int64_t>(b) * pa.R * pa.D + h * d + c;
 #pragma unroll
           for (int q = 0; q < TQ; ++q)
 #pragma unroll
             for (int j = 0; j < P; ++j) {
               const int i = (t0 + TQ * n + q) * P + j;
-              if (i < pa.R) erow[i] = acc[q][4 * g + u * P + j];
+              if (i < pa.R) erow[static_cast<int64_t>(i) * pa.D] = acc[q][4 * g + u * P + j];
             }
         }
       }
@@ -806,8 +808,7 @@ __global__ __launch_bounds__(256) void early_mix_kernel(ProjArgs pa) {
     float acc = 0.f;
 #pragma unroll
     for (int m = 0; m < H; ++m) acc = fmaf(a[m], ym[m], acc);
-    if (which == 2) pa.Vte[(static_cast<int64_t>(b * H + h) * d + c) * R + i] = acc;
-    else (which == 0 ? pa.Qe : pa.Ke)[(static_cast<int64_t>(b) * R + i) * D + h * d + c] = acc;
+    (which == 0 ? pa.Qe : which == 1 ? pa.Ke : pa.Ve)[(static_cast<int64_t>(b) * R + i) * D + h * d + c] = acc;
   }
 }
 
