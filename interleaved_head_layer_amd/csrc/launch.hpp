@@ -61,6 +61,7 @@ struct NtArgs {
   float* C;           // [I][ldc] fp32
   int I, J, K;
   int64_t ldc;
+  int jbase;          // fused mixing: global token of B's row 0 (the launcher splits tokens)
 };
 struct ProjArgs {
   const uint16_t* X;      // [B*N][D] bf16

@@ -301,7 +301,7 @@ __global__ __launch_bounds__(GThreads, 1) void gemm_mix_bf16_kernel(NtArgs g, Pr
   __shared__ __attribute__((aligned(16))) NtSmem<RBW> sm;
   gemm_tile<RBW>(g, sm, [&](floatx16 (&acc)[RBW][2], int i0, int j0, int wm, int wn) {
     const int lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5;
-    const int D = pa.D, d = pa.d, N = pa.N, M = g.J;
+    const int D = pa.D, d = pa.d, N = pa.N, M = pa.B * pa.N;
     const int which = i0 / D;                          // tiles never straddle Q / K / V
     const int c0 = ((i0 % D) + 32 * RBW * wm) / H;     // the wave's 8 channels: c0 .. c0 + 7
     const float* __restrict__ al = pa.alpha[which];
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(GThreads, 1) void gemm_mix_bf16_kernel(NtArgs g, Pr
     // into the fp32 first rows.
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int tok = j0 + 64 * wn + 32 * j + l32;
+      const int tok = g.jbase + j0 + 64 * wn + 32 * j + l32;
       const int b = tok / N, t = tok % N;
       if (__builtin_expect(__any(tok < M && t < pa.T0), false)) {
         if (tok < M && t < pa.T0) {
@@ -378,7 +378,7 @@ __global__ __launch_bounds__(GThreads, 1) void gemm_mix_bf16_kernel(NtArgs g, Pr
     };
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int tok = j0 + 64 * wn + 32 * j + l32;
+      const int tok = g.jbase + j0 + 64 * wn + 32 * j + l32;
       const bool ok = tok < M;
       const int b = tok / N, t = tok % N;
       if (which < 2) {
@@ -829,18 +829,26 @@ hipError_t launch_proj_bf16(const ProjArgs& pa, hipStream_t s, hipEvent_t ev_pre
     g.J = M;
     g.K = D;
     const int ti = pa.H == 20 ? 320 : 256;
-    const int64_t tiles = static_cast<int64_t>(3 * D / ti) * ((M + GTJ - 1) / GTJ);
-    if (static_cast<int64_t>(M) * D * 2 >= (int64_t{1} << 31) || static_cast<int64_t>(3) * D * D * 2 >= (int64_t{1} << 31))
-      return hipErrorInvalidValue;
-    const int key = pa.H * 8 + pa.P;
-    switch (key) {
-      case 16 * 8 + 1: hipLaunchKernelGGL((gemm_mix_bf16_kernel<16, 1>), dim3(tiles), dim3(GThreads), 0, s, g, pa); break;
-      case 16 * 8 + 2: hipLaunchKernelGGL((gemm_mix_bf16_kernel<16, 2>), dim3(tiles), dim3(GThreads), 0, s, g, pa); break;
-      case 20 * 8 + 1: hipLaunchKernelGGL((gemm_mix_bf16_kernel<20, 1>), dim3(tiles), dim3(GThreads), 0, s, g, pa); break;
-      case 20 * 8 + 2: hipLaunchKernelGGL((gemm_mix_bf16_kernel<20, 2>), dim3(tiles), dim3(GThreads), 0, s, g, pa); break;
-      default: return hipErrorInvalidValue;
+    // Buffer offsets are 32-bit: the weights must span < 2 GiB, the tokens are split into
+    // launches of < 2 GiB of X each (whole 256-token tiles).
+    if (static_cast<int64_t>(3) * D * D * 2 >= (int64_t{1} << 31)) return hipErrorInvalidValue;
+    const int64_t max_j = ((int64_t{1} << 31) - 1) / (static_cast<int64_t>(D) * 2) / GTJ * GTJ;
+    for (int64_t jb = 0; jb < M; jb += max_j) {
+      NtArgs c = g;
+      c.B = pa.X + jb * D;
+      c.J = static_cast<int>(std::min<int64_t>(max_j, M - jb));
+      c.jbase = static_cast<int>(jb);
+      const int64_t tiles = static_cast<int64_t>(3 * D / ti) * ((c.J + GTJ - 1) / GTJ);
+      const int key = pa.H * 8 + pa.P;
+      switch (key) {
+        case 16 * 8 + 1: hipLaunchKernelGGL((gemm_mix_bf16_kernel<16, 1>), dim3(tiles), dim3(GThreads), 0, s, c, pa); break;
+        case 16 * 8 + 2: hipLaunchKernelGGL((gemm_mix_bf16_kernel<16, 2>), dim3(tiles), dim3(GThreads), 0, s, c, pa); break;
+        case 20 * 8 + 1: hipLaunchKernelGGL((gemm_mix_bf16_kernel<20, 1>), dim3(tiles), dim3(GThreads), 0, s, c, pa); break;
+        case 20 * 8 + 2: hipLaunchKernelGGL((gemm_mix_bf16_kernel<20, 2>), dim3(tiles), dim3(GThreads), 0, s, c, pa); break;
+        default: return hipErrorInvalidValue;
+      }
+      if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     // the mixing is part of the GEMM; what is left of the mixing step is the fp32 mixing
     // of the first tokens
     if (ev_gemm && (e = hipEventRecord(ev_gemm, s)) != hipSuccess) return e;

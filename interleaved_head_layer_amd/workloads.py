@@ -139,6 +139,31 @@ def make_inputs(w: Workload) -> Dict[str, np.ndarray]:
     return {k: np.ascontiguousarray(v, dtype=np.float32) for k, v in out.items()}
 
 
+def make_params(w: Workload) -> Dict[str, np.ndarray]:
+    """Weights, mixing tensors and collapse map of workload ``w`` without X, for inputs too
+    large to draw in one array: drawn from PCG64 seeded with (seed, 0) in the order W_Q, W_K,
+    W_V, alpha^Q, alpha^K, alpha^V, R, with the distributions of ``make_inputs``."""
+    rng = np.random.Generator(np.random.PCG64([w.seed, 0]))
+    D, H, P = w.D, w.H, w.P
+    s = np.float32(1.0 / np.sqrt(D))
+    W = [rng.standard_normal((D, D), dtype=np.float32) * s for _ in range(3)]
+    sa = np.float32(1.0 / np.sqrt(H))
+    al = [rng.standard_normal((H, H, P), dtype=np.float32) * sa for _ in range(3)]
+    R = rng.standard_normal((H, H * P), dtype=np.float32) * np.float32(1.0 / np.sqrt(H * P))
+    if w.dtype == "bf16":
+        W = [round_to_bf16(a) for a in W]
+    out = dict(WQ=W[0], WK=W[1], WV=W[2], aQ=al[0], aK=al[1], aV=al[2], R=R)
+    return {k: np.ascontiguousarray(v, dtype=np.float32) for k, v in out.items()}
+
+
+def make_sequence(w: Workload, b: int) -> np.ndarray:
+    """X[b] ([N, D], N(0, 1), bf16-rounded for bf16 workloads) drawn on its own from PCG64
+    seeded with (seed, b + 1), so that any one sequence of a large batch can be redrawn."""
+    rng = np.random.Generator(np.random.PCG64([w.seed, b + 1]))
+    x = rng.standard_normal((w.N, w.D), dtype=np.float32)
+    return round_to_bf16(x) if w.dtype == "bf16" else x
+
+
 def make_stacked_qkv(B: int, PN: int, H: int, d: int, seed: int, scale: float = 1.0):
     """Draw fp16-representable stacked Q-bar, K-bar, V-bar of shape [B, PN, H, d] (interleaved rows).
 

@@ -10,6 +10,7 @@ query/key tiles (128/64 rows) and GEMM tiles (128) and end in ragged tails.  Ful
 workloads are launched exactly as the benchmark launches them and checked on sampled
 tokens, which the oracle computes exactly (only the keys those tokens can see).
 """
+import concurrent.futures
 import math
 import sys
 
@@ -129,6 +130,45 @@ def test_full_size_workload_sampled(name):
     rms = float(np.sqrt(np.mean(ref[np.isin(tokens, uniform)] ** 2)))
     check(gpu[tokens], ref, BF16_TOL, rms=rms, what=f"{name} ({len(tokens)} tokens)")
     assert np.all(np.isfinite(gpu))
+
+
+def test_fused_projection_beyond_2gib_of_x():
+    """X of 1025 x 1024 tokens x 1024 bf16 (2.15 GB) exceeds what one launch of the fused
+    projection GEMM addresses, so its tokens are split over two launches at token 1,048,320,
+    inside sequence 1023.  Checked on tokens on both sides of that split and in the first and
+    last sequences."""
+    w = wl.custom(1025, 1024, 1024, 16, 1, "causal", seed=4242)
+    note(w.describe())
+    prob = iha.make_problem(w.B, w.N, w.D, w.H, w.P, w.mask, w.window)
+    assert iha.iha_plan(prob) & iha.IHA_PLAN_MIX_FUSED
+    p = wl.make_params(w)
+    X = torch.empty(w.B, w.N, w.D, dtype=torch.bfloat16, device=DEV)
+    Xf = X.view(w.B * w.N, w.D)
+    assert X.numel() * 2 >= 2 ** 31
+    step = 64
+    with concurrent.futures.ThreadPoolExecutor(8) as ex:
+        for b0 in range(0, w.B, step):
+            blk = np.concatenate(list(ex.map(lambda b: wl.make_sequence(w, b), range(b0, min(w.B, b0 + step)))))
+            Xf[b0 * w.N:b0 * w.N + blk.shape[0]] = torch.from_numpy(blk).to(torch.bfloat16).to(DEV)
+    dev = lambda a, d: torch.from_numpy(a).to(DEV).to(d).contiguous()
+    bf, f32 = torch.bfloat16, torch.float32
+    out = iha.iha_forward(X, dev(p["WQ"], bf), dev(p["WK"], bf), dev(p["WV"], bf), dev(p["aQ"], f32),
+                          dev(p["aK"], f32), dev(p["aV"], f32), dev(p["R"], f32), w.H, w.P, w.mask,
+                          w.window)
+    del X, Xf
+    out = out.reshape(w.B * w.N, w.D)
+    split = 1048320
+    rng = np.random.default_rng(w.seed)
+    for b, local in [(0, [0, 1, 2, 517, 1023]),
+                     (1023, [0, 1, 765, 766, 767, 768, 769, 770, 1022, 1023]),
+                     (1024, [0, 1, 2, 3, 300, 1023])]:
+        local = np.unique(np.concatenate([local, rng.choice(w.N, 6, replace=False)]))
+        gpu = out[torch.from_numpy(b * w.N + local).to(DEV)].cpu().numpy().astype(np.float64)
+        ref = oracle.forward(wl.make_sequence(w, b)[None], p["WQ"], p["WK"], p["WV"], p["aQ"], p["aK"],
+                             p["aV"], p["R"], w.H, w.P, w.mask, w.window, tokens=local)
+        check(gpu, ref, BF16_TOL, what=f"sequence {b} tokens {local.tolist()}")
+    assert 1023 * w.N < split < 1024 * w.N
+    assert torch.isfinite(out).all().item()
 
 
 # --------------------------------------------------------------- attention step alone
