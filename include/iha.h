@@ -41,7 +41,7 @@
  * those fp32 projections in fp32, and the mixed Q/K/V and the attention
  * probabilities are stored as fp16 for the fp16 matrix cores (fp32
  * accumulation); softmax state, the per-head attention output and X_out are
- * fp32.  Under a causal or window mask the first 128 stacked rows of every
+ * fp32.  Under a causal or window mask the first 32 stacked rows of every
  * (b, h) see the fewest keys and have the largest outputs; their attention is
  * recomputed in fp32 from fp32 copies of their mixed queries, keys and values,
  * so that their absolute error matches the other rows'.

@@ -293,7 +293,6 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
   const int qt = (MASK == kMaskCausal) ? (nqt - 1 - qi) : qi;
   const int b = bh / H, h = bh % H;
   const int q0 = qt * ABM;
-  if (a.skip_first && qt == 0) return;  // rows recomputed elsewhere (whole workgroup)
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;

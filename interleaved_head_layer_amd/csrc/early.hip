@@ -4,11 +4,11 @@
 // Why: a stacked row that sees n keys has an output of magnitude about n^-1/2 (it averages
 // n value rows with softmax weights), while the fp16 intermediates of the main path carry a
 // fixed relative error.  The first rows see only a handful of keys, so their outputs, and
-// their absolute errors, are far above the typical output; the output error bound is set
-// by them.  These rows (the first 128, one query tile) are recomputed here in fp32 from the
-// fp32 copies of their projected and mixed queries, keys and values (written by the mixing
-// kernels), and overwrite those rows of P-bar after the main attention kernel.  Every later
-// row sees more than 128 keys.
+// their absolute errors, are far above the typical output.  The first kPreciseRows (32)
+// stacked rows of every (b, h) are recomputed here in fp32 from fp32 copies of their
+// projected and mixed queries, keys and values (written by the mixing step) into a
+// separate fp32 buffer that the collapse reads for those rows.  Row 32 and later see at
+// least 33 keys, so their fp16 errors are already several times below row 0's.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -25,15 +25,24 @@ namespace {
 // values, whose global loads are issued into registers before the score phase.
 // grid: (ceil(R / 32), H, B).
 constexpr int ERows = 32, EThreads = 512, EGroup = 16;
-constexpr int EStride = kPreciseRows + 4;  // floats per LDS row (float4-aligned, staggered banks)
+// LDS rows are padded by 4 floats (float4-aligned, consecutive rows on staggered banks).
+template <int DH>
+struct EarlySmem {
+  static constexpr int QS = (DH > kPreciseRows ? DH : kPreciseRows) + 4;  // Q rows, then P rows
+  static constexpr int KS = DH + 4;                                       // K[n][c]
+  static constexpr int VS = kPreciseRows + 4;                             // V^T[c][n]
+  float qs[ERows][QS];
+  float kv[kPreciseRows * KS > DH * VS ? kPreciseRows * KS : DH * VS];    // K, then V^T
+};
 
 template <int DH>
 __global__ __launch_bounds__(EThreads) void early_attn_kernel(EarlyArgs e, float* __restrict__ O,
                                                               int64_t o_bstride, int mask,
                                                               int window, float scale) {
-  static_assert(DH + 4 <= EStride, "row stride");
-  __shared__ __attribute__((aligned(16))) float qs[ERows][EStride];  // Q rows, then P rows
-  __shared__ __attribute__((aligned(16))) float kv[kPreciseRows][EStride];  // K[n][c] then V^T[c][n]
+  using Sm = EarlySmem<DH>;
+  __shared__ __attribute__((aligned(16))) Sm sm;
+  auto& qs = sm.qs;
+  float* kv = sm.kv;
   const int R = e.R, H = e.H, D = e.D;
   const int h = blockIdx.y, b = blockIdx.z;
   const int i0 = blockIdx.x * ERows;
@@ -85,7 +94,7 @@ __global__ __launch_bounds__(EThreads) void early_attn_kernel(EarlyArgs e, float
 #pragma unroll
   for (int q = 0; q < KPT; ++q) {
     const int x = tid + q * EThreads, n = x / C4;
-    if (n < nu * EGroup) *reinterpret_cast<floatx4*>(&kv[n][(x % C4) * 4]) = kreg[q];
+    if (n < nu * EGroup) *reinterpret_cast<floatx4*>(&kv[n * Sm::KS + (x % C4) * 4]) = kreg[q];
   }
   __syncthreads();
 
@@ -99,7 +108,7 @@ __global__ __launch_bounds__(EThreads) void early_attn_kernel(EarlyArgs e, float
 #pragma unroll
     for (int u = 0; u < kPreciseRows / EGroup; ++u) {
       if (u < nu) {
-        const floatx4 k4 = *reinterpret_cast<const floatx4*>(&kv[g + EGroup * u][c]);
+        const floatx4 k4 = *reinterpret_cast<const floatx4*>(&kv[(g + EGroup * u) * Sm::KS + c]);
         s[u] = fmaf(q4[0], k4[0], s[u]);
         s[u] = fmaf(q4[1], k4[1], s[u]);
         s[u] = fmaf(q4[2], k4[2], s[u]);
@@ -137,7 +146,7 @@ __global__ __launch_bounds__(EThreads) void early_attn_kernel(EarlyArgs e, float
     const int x = tid + q * EThreads;
     const int n = x / C4, c = (x % C4) * 4;
 #pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) kv[c + e4][n] = vreg[q][e4];
+    for (int e4 = 0; e4 < 4; ++e4) kv[(c + e4) * Sm::VS + n] = vreg[q][e4];
   }
   __syncthreads();
 
@@ -151,7 +160,7 @@ __global__ __launch_bounds__(EThreads) void early_attn_kernel(EarlyArgs e, float
     const floatx4 p4 = *reinterpret_cast<const floatx4*>(&qs[r][n]);
 #pragma unroll
     for (int u = 0; u < CU; ++u) {
-      const floatx4 v4 = *reinterpret_cast<const floatx4*>(&kv[g + EGroup * u][n]);
+      const floatx4 v4 = *reinterpret_cast<const floatx4*>(&kv[(g + EGroup * u) * Sm::VS + n]);
       acc[u] = fmaf(p4[0], v4[0], acc[u]);
       acc[u] = fmaf(p4[1], v4[1], acc[u]);
       acc[u] = fmaf(p4[2], v4[2], acc[u]);

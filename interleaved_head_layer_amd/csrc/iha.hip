@@ -242,12 +242,10 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
                   : 0;
   const float score_scale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
   at.qk_scale = score_scale;
-  static_assert(iha::kPreciseRows == 128, "the fp32 first rows are the fp16 kernel's query tile 0");
   if (bf16) {
     at.qk_scale = 1.f;  // the fp16 Q was stored pre-scaled
     at.qk_layout = qk_layout;
     at.Oh = reinterpret_cast<iha::half_t*>(ws + lay.pbar);  // fp16 stacked outputs
-    at.skip_first = lay.R > 0;  // rows 0 .. R-1 (query tile 0) come from the fp32 recomputation
     IHA_HIP(iha::launch_attn_f16(at, stream));
   } else {
     at.O = reinterpret_cast<float*>(ws + lay.pbar);

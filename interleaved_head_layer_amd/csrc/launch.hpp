@@ -44,7 +44,6 @@ struct AttnArgs {
   const void* Vt;  // [B][H][d][L]
   float* O;        // [B][L][H][d] fp32, or null with Oh
   half_t* Oh;      // fp16 kernel only: [B][L][H][d] fp16 output instead of O (may be null)
-  int skip_first;  // fp16 kernel only: query tile 0 (rows 0..127) is not computed
   unsigned* flag;  // may be null
   int B, L, H, d, mask, window;
   float qk_scale;     // multiplies q . k to give base-2 scores
@@ -109,7 +108,7 @@ struct EarlyArgs {
 // (O [B][L][H][d] with batch stride o_bstride).
 hipError_t launch_early_attn(const EarlyArgs& e, float* O, int64_t o_bstride, int mask, int window,
                              float scale, hipStream_t s);
-constexpr int kPreciseRows = 128;
+constexpr int kPreciseRows = 32;
 
 // Unstack + collapse + concatenation:
 //   out[tok][h*d + c] = sum_{h', j} R[h][h'*P + j] * Pbar[tok*P + j][h'][c]

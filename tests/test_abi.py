@@ -46,7 +46,7 @@ def test_workspace_size_covers_the_intermediates():
     M, rows = B * N, B * N * P
     need = 3 * D * D * 2 + M * 2 * D * 4 + M * D * 4      # transposed W, fp32 projections
     need += 4 * rows * D * 2                               # Q~, K~, V~^T, P-bar (fp16)
-    R = min(128, P * N)                                    # fp32 first rows (bf16, masked):
+    R = min(32, P * N)                                    # fp32 first rows (bf16, masked):
     need += 4 * B * R * D * 4                              # their q, k, v and outputs
     assert need <= n <= need + 16 * 256
     st, n_none = _ws(mask="none")
@@ -75,7 +75,7 @@ def test_plan_and_workspace_follow_the_fused_mixing(B, N, D, H, P, dtype, fused)
     if dtype == bd.IHA_BF16:
         stacked += 3 * D * D * 2                                  # transposed weights
     if dtype == bd.IHA_BF16:                                      # fp32 first rows (causal)
-        R = min(128, P * N)
+        R = min(32, P * N)
         stacked += 4 * B * R * D * 4                              # their q, k, v, outputs
         if fused:
             stacked += B * -(-R // P) * 3 * D * 4                 # their unmixed projections
