@@ -20,6 +20,7 @@ struct CollapseSrc {
   const half_t* Ph;
   const float* Pe;
   int R, N;
+  int T0;  // matrix-core kernel: a sequence's first T0 tokens include fp32 rows
 };
 
 // fp32 stacked outputs.  block: 256 threads = (256 / (d/4)) tokens x (d/4) channel quads.
@@ -165,6 +166,126 @@ __global__ __launch_bounds__(256) void collapse_h_kernel(CollapseSrc src, const 
     if (h < H) *reinterpret_cast<floatx4*>(dst + h * d) = acc[h];
 }
 
+// fp16 stacked outputs on the matrix cores (H <= 32, d = 64 or 128).  Per token the
+// collapse is the product out[h][c] = sum_q Rt[h][q] * Pbar[q][c] over the token's H*P stacked
+// values q = j*H + h' (Rt[h][q] = R[h][h'*P + j]); a wave computes one 32-channel block of
+// one token with v_mfma_f32_32x32x16_f16: A = Rt (rows h, zero for h >= H), B = the token's
+// stacked block, K = q in steps of 16 (zero past H*P).  R is split into fp16 hi + lo parts
+// (two products on the exact fp16 stacked values), so the result carries about 2^-22
+// relative rounding on top of fp32 accumulation.  The workgroup (d/32 waves) stages each
+// token's [H*P][d] fp16 block in LDS (row stride d + 4 halves: the operand reads of rows q
+// and q + 8 fall on disjoint banks) and reads B transposed, 8 consecutive q per lane; the
+// next token's block is loaded into registers while the current one is multiplied.
+// A token whose stacked rows include fp32 first rows (the first T0 tokens of a sequence) is
+// collapsed in fp32 on the vector units by a whole workgroup, a thread per (head, 4
+// channels): the first `ne` workgroups stride over those tokens, the others over the rest.
+template <int KS, int NW>
+__global__ __launch_bounds__(NW * 64) void collapse_mfma_kernel(CollapseSrc src, const float* __restrict__ R,
+                                                               float* __restrict__ out, int ntok, int H, int P,
+                                                               int d, int ne) {
+  constexpr int NT = NW * 64;
+  extern __shared__ __attribute__((aligned(16))) uint16_t pl[];  // [KS*16][d + 4]
+  const int HP = H * P, ld = d + 4, N = src.N, T0 = src.T0;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+
+  if (static_cast<int>(blockIdx.x) < ne) {
+    // First-row tokens: rows i < R from the fp32 rows Pe [B][R][H][d], the rest fp16.
+    const int nearly = (ntok / N) * T0;
+    for (int e = blockIdx.x; e < nearly; e += ne) {
+      const int tok = (e / T0) * N + e % T0, t = e % T0;
+      const int64_t eb = static_cast<int64_t>(tok / N) * src.R;
+      const int quads = d / 4;
+      for (int u = tid; u < H * quads; u += NT) {
+        const int h = u / quads, c4 = (u % quads) * 4;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+        for (int q = 0; q < HP; ++q) {
+          const int j = q / H, hp = q % H, i = t * P + j;
+          floatx4 pv;
+          if (i < src.R) {
+            pv = *reinterpret_cast<const floatx4*>(src.Pe + ((eb + i) * H + hp) * d + c4);
+          } else {
+            const half4 v = *reinterpret_cast<const half4*>(src.Ph + (static_cast<int64_t>(tok) * HP + q) * d + c4);
+            pv = floatx4{static_cast<float>(v[0]), static_cast<float>(v[1]), static_cast<float>(v[2]),
+                         static_cast<float>(v[3])};
+          }
+          const float r = R[h * HP + hp * P + j];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[c] = fmaf(r, pv[c], acc[c]);
+        }
+        *reinterpret_cast<floatx4*>(out + static_cast<int64_t>(tok) * H * d + h * d + c4) = acc;
+      }
+    }
+    return;
+  }
+  const int g0 = blockIdx.x - ne, ng = gridDim.x - ne;  // this workgroup among the fp16 ones
+
+  // Rows HP .. KS*16-1 stay zero (their A columns are zero too, but LDS must hold no NaN).
+  for (int i = HP * ld + tid; i < KS * 16 * ld; i += NT) pl[i] = 0;
+  half8 ah[KS], al[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int q = ks * 16 + 8 * hf + e;
+      const float v = (l32 < H && q < HP) ? R[l32 * HP + (q % H) * P + q / H] : 0.f;
+      ah[ks][e] = static_cast<half_t>(v);
+      al[ks][e] = static_cast<half_t>(v - static_cast<float>(ah[ks][e]));
+    }
+  const int c0 = w * 32;
+  const int cpr = d / 8;     // 16-byte chunks per stacked row
+  const int nch = HP * cpr;  // chunks per token (<= KS * NT)
+  // The workgroup's fp16 tokens: tok = g0 + k * ng with t >= T0.
+  auto next_tok = [&](int tok) {
+    for (tok += ng; tok < ntok && tok % N < T0; tok += ng) {
+    }
+    return tok;
+  };
+  int tok = g0;
+  if (tok < ntok && tok % N < T0) tok = next_tok(tok);
+  uint4 buf[KS];
+  auto load = [&](int tk) {
+    const uint4* blk = reinterpret_cast<const uint4*>(src.Ph + static_cast<int64_t>(tk) * HP * d);
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      if (k * NT + tid < nch) buf[k] = blk[k * NT + tid];
+  };
+  if (tok < ntok) load(tok);
+  while (tok < ntok) {
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const int ch = k * NT + tid;
+      if (ch < nch) {
+        uint2* dst = reinterpret_cast<uint2*>(pl + (ch / cpr) * ld + (ch % cpr) * 8);  // 8-byte aligned
+        dst[0] = make_uint2(buf[k].x, buf[k].y);
+        dst[1] = make_uint2(buf[k].z, buf[k].w);
+      }
+    }
+    __syncthreads();
+    const int nt = next_tok(tok);
+    if (nt < ntok) load(nt);
+    floatx16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      half8 b;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b[e] = __builtin_bit_cast(half_t, pl[(ks * 16 + 8 * hf + e) * ld + c0 + l32]);
+      acc = mfma32(ah[ks], b, acc);
+      acc = mfma32(al[ks], b, acc);
+    }
+    __syncthreads();  // the next token's staging overwrites the block
+    float* dst = out + static_cast<int64_t>(tok) * H * d + c0 + l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int h = 8 * (r >> 2) + 4 * hf + (r & 3);
+      if (h < H) dst[static_cast<int64_t>(h) * d] = acc[r];
+    }
+    tok = nt;
+  }
+}
+
 template <int HMAX, bool HALF>
 hipError_t launch_impl(const CollapseSrc& src, const float* R, float* out, int ntok, int H, int P, int d,
                        hipStream_t s) {
@@ -194,14 +315,36 @@ hipError_t launch_h(const CollapseSrc& src, const float* R, float* out, int ntok
 
 hipError_t launch_collapse(const float* Pbar, const float* R, float* out, int ntok, int H, int P,
                            int d, hipStream_t s) {
-  const CollapseSrc src{Pbar, nullptr, nullptr, 0, 1};
+  const CollapseSrc src{Pbar, nullptr, nullptr, 0, 1, 0};
   return launch_h<false>(src, R, out, ntok, H, P, d, s);
 }
 
 hipError_t launch_collapse_h(const half_t* Ph, const float* Pe, int Rrows, const float* R, float* out, int B,
                              int N, int H, int P, int d, hipStream_t s) {
-  const CollapseSrc src{nullptr, Ph, Pe, Rrows, N};
-  return launch_h<true>(src, R, out, B * N, H, P, d, s);
+  const int HP = H * P, KS = (HP + 15) / 16;
+  if (H > 32 || KS > 8 || (d != 64 && d != 128)) {
+    const CollapseSrc src{nullptr, Ph, Pe, Rrows, N, 0};
+    return launch_h<true>(src, R, out, B * N, H, P, d, s);
+  }
+  const CollapseSrc src{nullptr, Ph, Pe, Rrows, N, (Rrows + P - 1) / P};
+  const int ntok = B * N;
+  // A few workgroups for the first-row tokens, then about 8 fp16 tokens per workgroup.
+  const int ne = std::min(B * src.T0, 256);
+  const int grid = ne + std::max(1, std::min(ntok / 8, 256 * 8 - ne));
+  const size_t lds = static_cast<size_t>(KS) * 16 * (d + 4) * sizeof(uint16_t);
+  auto go = [&](auto kern, int threads) {
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, s, src, R, out, ntok, H, P, d, ne);
+  };
+  switch (KS * 4 + d / 64) {  // d / 64 in {1, 2}
+#define IHA_COLLAPSE_CASE(ks)                                                    \
+  case ks * 4 + 1: go(collapse_mfma_kernel<ks, 2>, 128); break;                  \
+  case ks * 4 + 2: go(collapse_mfma_kernel<ks, 4>, 256); break;
+    IHA_COLLAPSE_CASE(1) IHA_COLLAPSE_CASE(2) IHA_COLLAPSE_CASE(3) IHA_COLLAPSE_CASE(4)
+    IHA_COLLAPSE_CASE(5) IHA_COLLAPSE_CASE(6) IHA_COLLAPSE_CASE(7) IHA_COLLAPSE_CASE(8)
+#undef IHA_COLLAPSE_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace iha
