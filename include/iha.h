@@ -133,10 +133,11 @@ iha_status iha_forward(const iha_problem* prob, const void* X, const void* W_Q, 
 /* iha_forward that also records IHA_TIMED_EVENTS events on `stream` around its
  * steps: [0] start, [1] after the weight preparation (bf16: transpose; fp32:
  * mixing folded into the weights), [2] after the projection GEMMs, [3] after the
- * mixing (fp32: no separate mixing, recorded right after [2]; IHA_PLAN_MIX_FUSED:
- * only the fp32 mixing of the first tokens lies between [2] and [3]), [4] after the
- * attention kernel, [5] after the fp32 recomputation of the first stacked rows
- * (no work for IHA_F32 or IHA_MASK_NONE), [6] after the collapse.
+ * mixing (fp32 and IHA_PLAN_MIX_FUSED: no separate mixing, recorded right after
+ * [2]), [4] after the attention launch (for bf16 inputs under a mask it also
+ * computes the first stacked rows in fp32), [5] recorded right after [4] (kept
+ * for a stable event count), [6] after the collapse.  Every event record adds a
+ * gap of roughly 10 us between the kernels it separates.
  * The events are created by the caller (hipEventCreate) and must not be NULL;
  * a NULL array or entry returns IHA_ERR_INVALID_ARG before any launch. */
 #define IHA_TIMED_EVENTS 7

@@ -277,6 +277,133 @@ __device__ __forceinline__ void attn_tile(bool edge, const half_t* __restrict__ 
   }
 }
 
+// ------------------------------------------------------------ fp32 first rows
+// The first R <= kPreciseRows stacked rows of a (b, h) see the fewest keys, so their outputs
+// are the largest and the fp16 roundings of the tiled kernel weigh most there (an output that
+// averages n value rows is about n^-1/2 in size).  bf16 forwards compute them again in fp32
+// on B*H extra workgroups at the end of the fp16 kernel's grid (one per (b, h), 256
+// threads).  Their mixed queries, keys and values come as fp32 copies, or are mixed here in
+// fp32 from the unmixed projections of the first tokens (Algorithm 1's mixing, one head h).
+// Row i sees keys i' <= i (causal) or i - window < i' <= i, so only keys < R take part.
+// Thread t owns row r = t / 8 and lane g = t % 8 of the row's group: the scores of keys
+// g + 8u, then output channels g + 8u; a row's maximum and sum are 8-lane shuffles.
+constexpr int EGroup = 8;
+template <int DH, int MASK>
+__device__ __forceinline__ void first_rows(const AttnArgs& a, int b, int h, float* smem) {
+  constexpr int ER = kPreciseRows;                                 // rows and keys, at most
+  constexpr int QS = (DH > ER ? DH : ER) + 4, KS = DH + 4;          // padded LDS rows (floats)
+  constexpr int C4 = DH / 4, NU = ER / EGroup, CU = DH / EGroup;
+  static_assert(ER * QS + 2 * ER * KS + 3 * 20 * 2 <= sizeof(AttnSmem<DH>) / 4, "LDS");
+  float(*qs)[QS] = reinterpret_cast<float(*)[QS]>(smem);          // Q rows, then probabilities
+  float(*ks)[KS] = reinterpret_cast<float(*)[KS]>(smem + ER * QS);  // K rows
+  float(*vs)[KS] = reinterpret_cast<float(*)[KS]>(smem + ER * QS + ER * KS);  // V rows
+  const int R = a.R, H = a.H, D = H * DH, tid = threadIdx.x, r = tid / EGroup, g = tid % EGroup;
+  const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+  if (a.Ye) {
+    // Q~_{h,j}[t][c] = sum_m alpha[m][h][j] Y^(m)[t][c] for rows i = t*P + j < R; Y^(m)[t][c]
+    // sits at Ye[b][t][which*D + fused_row(c, m)], four heads m at a time contiguous.  A
+    // thread takes (which, t, 4 channels) items and issues all H loads of one at once.
+    const int P = a.P, T0 = a.T0, per = T0 * C4;
+    float* as = smem + ER * QS + 2 * ER * KS;  // [which][m < 20][j < 2]: alpha[m][h][j], zero padded
+    if (tid < 3 * 20 * 2) {
+      const int which = tid / 40, m = (tid / 2) % 20, j = tid % 2;
+      const float* al = which == 0 ? a.alpha[0] : which == 1 ? a.alpha[1] : a.alpha[2];
+      as[tid] = m < H && j < P ? al[(m * H + h) * P + j] : 0.f;
+    }
+    __syncthreads();
+    for (int it = tid; it < 3 * per; it += AThreads) {
+      const int which = it / per, t = (it % per) / C4, c = (it % C4) * 4;
+      const float* yt = a.Ye + (static_cast<int64_t>(b) * T0 + t) * 3 * D + which * D;
+      floatx4 y[5][4];  // [m / 4][e][m % 4]; groups past H repeat the last one (weight zero)
+#pragma unroll
+      for (int m4 = 0; m4 < 5; ++m4)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          y[m4][e] = *reinterpret_cast<const floatx4*>(yt + fused_row(c + e, 4 * min(m4, H / 4 - 1), H));
+      const float* aw = as + which * 40;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {  // P <= 2 on this path
+        const int n = t * P + j;
+        if (j >= P || n >= R) break;
+        floatx4 acc = z;
+#pragma unroll
+        for (int m4 = 0; m4 < 5; ++m4)
+#pragma unroll
+          for (int mm = 0; mm < 4; ++mm) {
+            const float alpha = aw[(4 * m4 + mm) * 2 + j];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = fmaf(alpha, y[m4][e][mm], acc[e]);
+          }
+        float* row = which == 0 ? &qs[n][c] : which == 1 ? &ks[n][c] : &vs[n][c];
+        *reinterpret_cast<floatx4*>(row) = acc;
+      }
+    }
+  } else {
+    const int64_t base = static_cast<int64_t>(b) * R * D + h * DH;
+    for (int it = tid; it < ER * C4; it += AThreads) {
+      const int n = it / C4, c = (it % C4) * 4;
+      const int64_t off = base + static_cast<int64_t>(n) * D + c;
+      *reinterpret_cast<floatx4*>(&qs[n][c]) = n < R ? *reinterpret_cast<const floatx4*>(a.Qe + off) : z;
+      *reinterpret_cast<floatx4*>(&ks[n][c]) = n < R ? *reinterpret_cast<const floatx4*>(a.Ke + off) : z;
+      *reinterpret_cast<floatx4*>(&vs[n][c]) = n < R ? *reinterpret_cast<const floatx4*>(a.Ve + off) : z;
+    }
+  }
+  __syncthreads();
+  float sc[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) sc[u] = 0.f;
+#pragma unroll 4
+  for (int c = 0; c < DH; c += 4) {
+    const floatx4 q4 = *reinterpret_cast<const floatx4*>(&qs[r][c]);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const floatx4 k4 = *reinterpret_cast<const floatx4*>(&ks[g + EGroup * u][c]);
+      sc[u] = fmaf(q4[0], k4[0], sc[u]);
+      sc[u] = fmaf(q4[1], k4[1], sc[u]);
+      sc[u] = fmaf(q4[2], k4[2], sc[u]);
+      sc[u] = fmaf(q4[3], k4[3], sc[u]);
+    }
+  }
+  // Rows and keys >= R were never written: their scores are discarded here and their
+  // probabilities are zero.
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int k = g + EGroup * u;
+    const bool vis = k < R && k <= r && (MASK != kMaskWindow || k > r - a.window);
+    sc[u] = vis ? sc[u] * a.escale : -__builtin_inff();
+    mx = fmaxf(mx, sc[u]);
+  }
+#pragma unroll
+  for (int off = EGroup / 2; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, EGroup));
+  float sum = 0.f;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    sc[u] = mx == -__builtin_inff() ? 0.f : fast_exp2(sc[u] - mx);  // exp2(-inf) = 0
+    sum += sc[u];
+  }
+#pragma unroll
+  for (int off = EGroup / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, EGroup);
+  const float inv = sum > 0.f ? 1.f / sum : 0.f;
+  __syncthreads();  // every thread is done reading Q
+#pragma unroll
+  for (int u = 0; u < NU; ++u) qs[r][g + EGroup * u] = sc[u];
+  __syncthreads();
+  float acc[CU];
+#pragma unroll
+  for (int u = 0; u < CU; ++u) acc[u] = 0.f;
+  for (int n = 0; n < R; ++n) {
+    const float p = qs[r][n];
+#pragma unroll
+    for (int u = 0; u < CU; ++u) acc[u] = fmaf(p, vs[n][g + EGroup * u], acc[u]);
+  }
+  if (r < R) {
+    float* dst = a.Pe + static_cast<int64_t>(b) * R * D + static_cast<int64_t>(r) * D + h * DH;
+#pragma unroll
+    for (int u = 0; u < CU; ++u) dst[g + EGroup * u] = acc[u] * inv;
+  }
+}
+
 template <int DH, int MASK, bool DIRECT>
 __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) AttnSmem<DH> sm;
@@ -285,9 +412,18 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
   const int L = a.L, H = a.H, window = a.window;
   const int nqt = (L + ABM - 1) / ABM;
 
+  // The last B*H workgroups (they fill the slots the tiled workgroups leave idle at the end):
+  // fp32 first rows of one (b, h) each.
+  const int ne = MASK != kMaskNone && a.R > 0 ? a.B * H : 0;
+  const int nmain = static_cast<int>(gridDim.x) - ne;
+  if (MASK != kMaskNone && static_cast<int>(blockIdx.x) >= nmain) {
+    const int e = blockIdx.x - nmain;
+    first_rows<DH, MASK>(a, e / H, e % H, reinterpret_cast<float*>(&sm));
+    return;
+  }
   // Flat id -> (b, h, query tile); consecutive logical ids share (b, h) and run on one
   // XCD.  Causal rows get longer with the tile index, so causal launches them longest first.
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int lid = xcd_remap(blockIdx.x, nmain);
   const int bh = lid / nqt;
   const int qi = lid % nqt;
   const int qt = (MASK == kMaskCausal) ? (nqt - 1 - qi) : qi;
@@ -468,7 +604,9 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnArgs a) {
 template <int DH, int MASK>
 hipError_t launch_f16_impl(const AttnArgs& a, hipStream_t s) {
   const int nqt = (a.L + ABM - 1) / ABM;
-  const dim3 grid(nqt * a.H * a.B);
+  if (a.R < 0 || a.R > kPreciseRows || (a.R > 0 && MASK == kMaskNone)) return hipErrorInvalidValue;
+  const int ne = a.R > 0 ? a.H * a.B : 0;  // first-row workgroups
+  const dim3 grid(ne + nqt * a.H * a.B);
   // Buffer loads: 16-byte aligned V^T rows (L % 8 == 0) and 32-bit byte offsets within one
   // batch's K and one head's V^T.
   const bool direct = a.L % 8 == 0 && static_cast<int64_t>(a.L) * a.H * DH * 2 < (int64_t{1} << 31);

@@ -39,6 +39,13 @@ __device__ __forceinline__ floatx16 mfma32(half8 a, half8 b, floatx16 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Row of (channel c, source head m) of one weight matrix in the fused layout (H = 16 or 20):
+// 8-channel groups of 8H rows; in a group, channel cl's heads m < 16 at rows cl*16 + m and
+// (H = 20) its heads 16..19 at rows 128 + cl*4 + (m - 16).
+__device__ __forceinline__ int fused_row(int c, int m, int H) {
+  return (c >> 3) * (8 * H) + (m < 16 ? (c & 7) * 16 + m : 128 + (c & 7) * 4 + (m - 16));
+}
+
 // XCD-aware remap of a flat workgroup id: the hardware deals consecutive
 // workgroups round-robin to the 8 XCDs, so consecutive logical ids are given to
 // the same XCD (its own L2) instead.

@@ -22,7 +22,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
 struct Layout {
-  size_t flag, wt, yqk, yvt, ye, q, k, vt, pbar, pe, qe, ke, vte, total;
+  size_t flag, wt, yqk, yvt, q, k, vt, pbar, pe, qe, ke, vte, ye, total;
   int R;  // precise first stacked rows (0 when unused)
 };
 
@@ -81,17 +81,20 @@ Layout layout_of(const iha_problem& p) {
   L.k = take(act * e);
   L.vt = take(act * e);
   L.pbar = take(act * e);  // stacked attention outputs: fp16 (bf16 inputs) or fp32
-  // bf16 inputs under a causal or window mask: fp32 copies of the first rows' queries, keys
-  // and values, and their fp32 attention outputs.
+  // bf16 inputs under a causal or window mask: the first rows' fp32 attention outputs, and
+  // fp32 copies of their mixed queries, keys and values (fused path: the unmixed fp32
+  // projections of the first tokens instead, mixed by the attention launch).
   if (p.dtype == IHA_BF16 && p.mask != IHA_MASK_NONE) {
     const int64_t R = std::min<int64_t>(iha::kPreciseRows, p.P * p.N);
     L.R = static_cast<int>(R);
-    L.qe = take(static_cast<size_t>(p.B) * R * p.D * 4);
-    L.ke = take(static_cast<size_t>(p.B) * R * p.D * 4);
-    L.vte = take(static_cast<size_t>(p.B) * R * p.D * 4);
     L.pe = take(static_cast<size_t>(p.B) * R * p.D * 4);
-    if (iha::fused_shape(p.H, p.D, p.P))  // unmixed projections of the first tokens
+    if (iha::fused_shape(p.H, p.D, p.P)) {
       L.ye = take(static_cast<size_t>(p.B) * ((R + p.P - 1) / p.P) * 3 * p.D * 4);
+    } else {
+      L.qe = take(static_cast<size_t>(p.B) * R * p.D * 4);
+      L.ke = take(static_cast<size_t>(p.B) * R * p.D * 4);
+      L.vte = take(static_cast<size_t>(p.B) * R * p.D * 4);
+    }
   }
   L.total = off;
   return L;
@@ -171,11 +174,12 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
     pa.Q = reinterpret_cast<iha::half_t*>(ws + lay.q);
     pa.K = reinterpret_cast<iha::half_t*>(ws + lay.k);
     pa.Vt = reinterpret_cast<iha::half_t*>(ws + lay.vt);
-    if (lay.R > 0) {
+    if (lay.R > 0 && fused) {
+      pa.Ye = reinterpret_cast<float*>(ws + lay.ye);
+    } else if (lay.R > 0) {
       pa.Qe = reinterpret_cast<float*>(ws + lay.qe);
       pa.Ke = reinterpret_cast<float*>(ws + lay.ke);
       pa.Ve = reinterpret_cast<float*>(ws + lay.vte);
-      pa.Ye = reinterpret_cast<float*>(ws + lay.ye);
     }
     pa.B = B;
     pa.N = N;
@@ -246,27 +250,32 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
     at.qk_scale = 1.f;  // the fp16 Q was stored pre-scaled
     at.qk_layout = qk_layout;
     at.Oh = reinterpret_cast<iha::half_t*>(ws + lay.pbar);  // fp16 stacked outputs
+    if (lay.R > 0) {
+      // The first stacked rows again, in fp32, by extra workgroups of the same launch (their
+      // outputs are the largest).
+      if (iha::fused_shape(H, D, P)) {
+        at.Ye = reinterpret_cast<const float*>(ws + lay.ye);
+        at.alpha[0] = alpha_Q;
+        at.alpha[1] = alpha_K;
+        at.alpha[2] = alpha_V;
+      } else {
+        at.Qe = reinterpret_cast<const float*>(ws + lay.qe);
+        at.Ke = reinterpret_cast<const float*>(ws + lay.ke);
+        at.Ve = reinterpret_cast<const float*>(ws + lay.vte);
+      }
+      at.Pe = reinterpret_cast<float*>(ws + lay.pe);
+      at.R = lay.R;
+      at.P = P;
+      at.T0 = (lay.R + P - 1) / P;
+      at.escale = score_scale;
+    }
     IHA_HIP(iha::launch_attn_f16(at, stream));
   } else {
     at.O = reinterpret_cast<float*>(ws + lay.pbar);
     IHA_HIP(iha::launch_attn_f32(at, stream));
   }
   if (ev) IHA_HIP(hipEventRecord(ev[4], stream));
-  if (lay.R > 0) {
-    // The first stacked rows again, with fp32 intermediates (their outputs are the largest).
-    iha::EarlyArgs ea{};
-    ea.Qe = reinterpret_cast<float*>(ws + lay.qe);
-    ea.Ke = reinterpret_cast<float*>(ws + lay.ke);
-    ea.Ve = reinterpret_cast<float*>(ws + lay.vte);
-    ea.B = B;
-    ea.H = H;
-    ea.D = D;
-    ea.d = d;
-    ea.R = lay.R;
-    IHA_HIP(iha::launch_early_attn(ea, reinterpret_cast<float*>(ws + lay.pe), static_cast<int64_t>(lay.R) * H * d,
-                                   p.mask, std::min(at.window, lay.R), score_scale, stream));
-  }
-  if (ev) IHA_HIP(hipEventRecord(ev[5], stream));
+  if (ev) IHA_HIP(hipEventRecord(ev[5], stream));  // (first rows: part of the attention launch)
 
   // Steps 4-5: unstack, collapse with R, concatenate heads.
   if (bf16)

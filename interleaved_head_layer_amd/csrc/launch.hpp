@@ -36,6 +36,10 @@ hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s);
 constexpr int kQKRowMajor = 0;  // [B][L][H][d]
 constexpr int kQKChunked = 1;   // [B][H][d/8][L][8]: 16-byte d-chunks, contiguous over rows
 
+// bf16 inputs under a causal or window mask: the first kPreciseRows stacked rows of every
+// (b, h) see the fewest keys and have the largest outputs; they are computed again in fp32.
+constexpr int kPreciseRows = 32;
+
 // Masked attention over the stacked sequence: O = softmax_2(s) V with base-2 scores
 // s = (q . k) * qk_scale.
 struct AttnArgs {
@@ -49,6 +53,19 @@ struct AttnArgs {
   float qk_scale;     // multiplies q . k to give base-2 scores
   int64_t o_bstride;  // elements between batches of O (0: L*H*d)
   int qk_layout;      // kQKRowMajor or kQKChunked
+  // fp16 kernel, causal or window mask, R > 0: B*H extra workgroups of the same launch
+  // compute the first R (<= kPreciseRows) stacked rows of every (b, h) in fp32 into Pe
+  // [B][R][H][d] (base-2 scores scaled by escale), from fp32 copies Qe, Ke, Ve [B][R][H][d]
+  // or, when Ye is set, from the unmixed fp32 projections Ye [B][T0][3D] of the first
+  // T0 = ceil(R / P) tokens (fused row order, H = 16 or 20) mixed here with alpha[3].
+  const float* Qe;
+  const float* Ke;
+  const float* Ve;
+  const float* Ye;
+  const float* alpha[3];
+  float* Pe;
+  int R, P, T0;
+  float escale;
 };
 hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
@@ -72,10 +89,11 @@ struct ProjArgs {
   half_t* Q;              // [B][P*N][H][d] fp16, multiplied by qscale
   half_t* K;
   half_t* Vt;             // [B][H][d][P*N] fp16
-  float* Qe;              // fp32 copies of the first R stacked rows (or null)
+  float* Qe;              // unfused path: fp32 copies of the first R stacked rows (or null)
   float* Ke;
   float* Ve;
-  float* Ye;              // fused path: [B][T0][3D] unmixed fp32 projections of the first tokens
+  float* Ye;              // fused path: [B][T0][3D] unmixed fp32 projections of the first
+                          // T0 tokens (rows as permuted by fused_row), or null
   int B, N, D, H, d, P, R;
   int T0;                 // ceil(R / P): tokens whose pseudo-tokens include a first row
   float qscale;           // factor applied to the fp16 Q (the base-2 score scale)
@@ -92,23 +110,9 @@ inline bool fused_shape(int64_t H, int64_t D, int64_t P) {
 // Q~ and K~ are then written in the chunked layout [B][H][d/8][P*N][8], else row-major.
 bool proj_fused(const ProjArgs& pa);
 // ev_prep (may be null) is recorded after the weight transpose, ev_gemm after the projection
-// GEMMs (with the fused path: after the fused kernel, the mixing included, before the fp32
-// mixing of the first tokens).
+// GEMMs (with the fused path: after the fused kernel, the mixing included).
 hipError_t launch_proj_bf16(const ProjArgs& pa, hipStream_t s, hipEvent_t ev_prep, hipEvent_t ev_gemm);
 
-// fp32 copies of the first R stacked rows (R = min(128, P*N)) of every (b, h) for bf16
-// inputs under a causal or window mask: Qe, Ke, Ve [B][R][H][d].
-struct EarlyArgs {
-  const float* Qe;
-  const float* Ke;
-  const float* Ve;
-  int B, H, D, d, R;
-};
-// fp32 attention of those rows (causal / window), written into O rows < R
-// (O [B][L][H][d] with batch stride o_bstride).
-hipError_t launch_early_attn(const EarlyArgs& e, float* O, int64_t o_bstride, int mask, int window,
-                             float scale, hipStream_t s);
-constexpr int kPreciseRows = 32;
 
 // Unstack + collapse + concatenation:
 //   out[tok][h*d + c] = sum_{h', j} R[h][h'*P + j] * Pbar[tok*P + j][h'][c]

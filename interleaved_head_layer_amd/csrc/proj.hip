@@ -19,13 +19,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-// Row of (channel c, source head m) of one weight matrix in the fused layout (H = 16 or 20):
-// 8-channel groups of 8H rows; in a group, channel cl's heads m < 16 at rows cl*16 + m and
-// (H = 20) its heads 16..19 at rows 128 + cl*4 + (m - 16).
-__device__ __forceinline__ int fused_row(int c, int m, int H) {
-  return (c >> 3) * (8 * H) + (m < 16 ? (c & 7) * 16 + m : 128 + (c & 7) * 4 + (m - 16));
-}
-
 // ------------------------------------------------------------------- W transpose
 // grid: (D/64, D/64, 3); block 256.  64x64 tiles through LDS, 16-byte global loads and
 // stores (8 bf16 per thread and access).  With `cm`, column n = m*d + c of W (head m,
@@ -239,8 +232,8 @@ __global__ __launch_bounds__(GThreads, 1) void gemm_nt_bf16_kernel(NtArgs g) {
 // fp32 accumulation, ~2^-21 relative).  Outputs:
 //   V~^T [B][H][d][P*N]           (P consecutive fp16 per lane and head),
 //   Q~, K~ [B][H][d/8][P*N][8]    (a wave's 8 channels form one 16-byte chunk per row),
-// plus the unmixed fp32 projections of the first tokens (mixed by early_mix_kernel); the
-// fp32 projections of all tokens never reach HBM.
+// plus the unmixed fp32 projections of the first tokens (Ye, mixed in fp32 by the
+// attention launch); the fp32 projections of the other tokens never reach HBM.
 __device__ __forceinline__ void split_f16(const floatx16& y, int cs, half8& bh, half8& bl) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -344,8 +337,8 @@ __global__ __launch_bounds__(GThreads, 1) void gemm_mix_bf16_kernel(NtArgs g, Pr
         }
     }
     // The first tokens' raw fp32 projections (rare column blocks holding a sequence's first
-    // T0 tokens) go to Ye[b][t][which*D + row] (row as permuted); early_mix_kernel mixes them
-    // into the fp32 first rows.
+    // T0 tokens) go to Ye[b][t][which*D + row] (row as permuted); the attention launch mixes
+    // them in fp32 into the first rows.
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int tok = g.jbase + j0 + 64 * wn + 32 * j + l32;
@@ -784,34 +777,6 @@ void launch_mix(const ProjArgs& pa, hipStream_t s) {
 
 }  // namespace
 
-// fp32 first rows of the fused path: the mixing of the unmixed fp32 projections Ye of each
-// sequence's first T0 tokens (fp32 FMAs).  One thread per (b, t, which, h, c); grid
-// (D / 256, B * T0 * 3).  The H = 16 source values and coefficients are all loaded up front.
-template <int H>
-__global__ __launch_bounds__(256) void early_mix_kernel(ProjArgs pa) {
-  const int d = pa.d, D = pa.D, P = pa.P, R = pa.R, T0 = pa.T0;
-  const int hc = blockIdx.x * 256 + threadIdx.x;
-  const int which = blockIdx.y % 3, bt = blockIdx.y / 3;
-  const int t = bt % T0, b = bt / T0;
-  const int h = hc / d, c = hc % d;
-  const float* __restrict__ y = pa.Ye + static_cast<int64_t>(bt) * 3 * D + which * D;
-  const float* __restrict__ al = pa.alpha[which];
-  float ym[H];
-#pragma unroll
-  for (int m = 0; m < H; ++m) ym[m] = y[fused_row(c, m, H)];
-  for (int j = 0; j < P; ++j) {
-    const int i = t * P + j;
-    if (i >= R) break;
-    float a[H];
-#pragma unroll
-    for (int m = 0; m < H; ++m) a[m] = al[(m * H + h) * P + j];
-    float acc = 0.f;
-#pragma unroll
-    for (int m = 0; m < H; ++m) acc = fmaf(a[m], ym[m], acc);
-    (which == 0 ? pa.Qe : which == 1 ? pa.Ke : pa.Ve)[(static_cast<int64_t>(b) * R + i) * D + h * d + c] = acc;
-  }
-}
-
 bool proj_fused(const ProjArgs& pa) { return fused_shape(pa.H, pa.D, pa.P); }
 
 hipError_t launch_proj_bf16(const ProjArgs& pa, hipStream_t s, hipEvent_t ev_prep, hipEvent_t ev_gemm) {
@@ -849,15 +814,8 @@ hipError_t launch_proj_bf16(const ProjArgs& pa, hipStream_t s, hipEvent_t ev_pre
       }
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    // the mixing is part of the GEMM; what is left of the mixing step is the fp32 mixing
-    // of the first tokens
+    // the mixing (first rows' fp32 copies included) is part of the GEMM
     if (ev_gemm && (e = hipEventRecord(ev_gemm, s)) != hipSuccess) return e;
-    if (pa.R > 0) {
-      const dim3 eg(D / 256, pa.B * pa.T0 * 3);
-      if (pa.H == 20) hipLaunchKernelGGL(early_mix_kernel<20>, eg, dim3(256), 0, s, pa);
-      else hipLaunchKernelGGL(early_mix_kernel<16>, eg, dim3(256), 0, s, pa);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
     return hipSuccess;
   }
   NtArgs g1{};  // Y_QK = X * Wt_QK^T

@@ -76,9 +76,11 @@ def test_plan_and_workspace_follow_the_fused_mixing(B, N, D, H, P, dtype, fused)
         stacked += 3 * D * D * 2                                  # transposed weights
     if dtype == bd.IHA_BF16:                                      # fp32 first rows (causal)
         R = min(32, P * N)
-        stacked += 4 * B * R * D * 4                              # their q, k, v, outputs
+        stacked += B * R * D * 4                                  # their outputs, and
         if fused:
-            stacked += B * -(-R // P) * 3 * D * 4                 # their unmixed projections
+            stacked += B * -(-R // P) * 3 * D * 4                 # their tokens' projections
+        else:
+            stacked += 3 * B * R * D * 4                          # their q, k, v
     fp32_proj = B * N * 3 * D * 4
     if fused:
         assert stacked <= n <= stacked + 16 * 256
