@@ -104,6 +104,11 @@ SMALL = [
     (1, 128, 1024, 16, 1, "window", 21, "bf16"),     # H = 16, P = 1 fused
     (2, 256, 256, 4, 2, "window", None, "bf16"),     # W_s = 64: one key tile per query tile
     (4, 512, 512, 4, 2, "window", 300, "bf16"),      # window edges inside key tiles
+    # fewer stacked rows than the fp32 first rows (P*N < 32) on the fused path
+    (2, 10, 1024, 16, 2, "causal", None, "bf16"),    # R = 20 rows, 10 first tokens
+    (3, 7, 1280, 20, 1, "window", 3, "bf16"),        # H = 20, R = 7, window inside them
+    (1, 77, 1024, 16, 1, "window", 50, "bf16"),      # L = 77: register-copy attention path
+    (2, 45, 2560, 20, 2, "causal", None, "bf16"),    # L = 90 (not a multiple of 8), H = 20
 ]
 
 
