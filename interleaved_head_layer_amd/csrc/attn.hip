@@ -245,7 +245,14 @@ __device__ __forceinline__ void attn_tile(bool edge, const half_t* __restrict__ 
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmaxf(fmaxf(mx, __uint_as_float(sw[0])), __uint_as_float(sw[1]));
     }
-    const bool need = unset ? (mx > -__builtin_inff()) : (mx > 0.f);
+    // Each row decides from its own scores: a row without an offset takes its maximum; a row
+    // with one moves it only if one of its two lane sums exceeded 2^12 (not merely because
+    // another row of the wave needed the slow path), so rows never affect one another's
+    // rounding.  (The swap returns this lane's and the other lane's sum in an order that
+    // depends on the lane half; their maximum does not care.)
+    const auto tw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tsum), __float_as_uint(tsum), false, false);
+    const float thi = fmaxf(__uint_as_float(tw[0]), __uint_as_float(tw[1]));
+    const bool need = unset ? (mx > -__builtin_inff()) : !(thi <= kTileSumMax);
     const float delta = need ? mx : 0.f;
     const float alpha = !need ? 1.f : unset ? 0.f : fast_exp2(-mx);
     st.l *= alpha;

@@ -207,8 +207,11 @@ def test_bitwise_deterministic():
 
 
 @pytest.mark.parametrize("mask", ["causal", "window"])
-def test_future_perturbation_leaves_past_bitwise(mask):
-    """Textbook section 5.4: changing inputs after token t0 leaves outputs up to t0 unchanged."""
+@pytest.mark.parametrize("scale", [1.5, 6.0])
+def test_future_perturbation_leaves_past_bitwise(mask, scale):
+    """Textbook section 5.4: changing inputs after token t0 leaves outputs up to t0 unchanged,
+    bit for bit, also when the changed rows (scale 6: scores ~36x larger) drive the waves
+    they share with earlier rows through the softmax's offset updates."""
     w = wl.custom(1, 400, 256, 2, 2, mask, seed=5, window=64 if mask == "window" else None)
     note(w.describe())
     x = wl.make_inputs(w)
@@ -216,7 +219,7 @@ def test_future_perturbation_leaves_past_bitwise(mask):
     x2 = dict(x)
     X2 = x["X"].copy()
     t0 = 150
-    X2[:, t0 + 1:] = wl.round_to_bf16(X2[:, t0 + 1:] * 1.5 + 0.25)
+    X2[:, t0 + 1:] = wl.round_to_bf16(X2[:, t0 + 1:] * scale + 0.25)
     x2["X"] = X2
     b = gpu_forward(w, x2)
     assert np.array_equal(a[:, :t0 + 1], b[:, :t0 + 1])
