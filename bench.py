@@ -2,7 +2,7 @@
 """Throughput of the IHA forward pass on one MI355X.
 
 A step is one whole forward (weight transpose, projection GEMMs, mixing, attention,
-first-rows recomputation, collapse) over one batch of synthetic inputs that are resident in
+first rows, collapse) over one batch of synthetic inputs that are resident in
 HBM before timing.
 Prints one JSON line: pseudo-tokens/s for the whole forward (K plain forwards back to back),
 per-step times from HIP events recorded on the launch stream between the kernels of a second

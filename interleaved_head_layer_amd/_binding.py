@@ -124,8 +124,9 @@ def iha_forward(X, W_Q, W_K, W_V, alpha_Q, alpha_K, alpha_V, R, H: int, P: int, 
 
     ``events``: optional list of TIMED_EVENTS (7) torch.cuda.Event(enable_timing=True),
     recorded on the current stream at: start, after the weight preparation, after the
-    projection GEMMs, after the mixing, after attention, after the first-rows
-    recomputation, after the collapse."""
+    projection GEMMs, after the mixing (empty when the mixing runs in the GEMM), after the
+    attention launch (which also computes the fp32 first rows), again right after it (kept
+    for a stable count), after the collapse.  Each record adds a gap of about 10 us."""
     import torch
     if X.dim() != 3:
         raise ValueError("X must be [B, N, D]")
