@@ -173,7 +173,7 @@ def main():
                     help="first run a plain device copy of MIB MiB (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the forward runs on one GPU; --gpus {args.gpus} is not supported "
               "(the forward shards by sequence across GPUs with no exchange)",
               file=sys.stderr)
         sys.exit(2)
