@@ -112,10 +112,11 @@ iha_status iha_workspace_bytes(const iha_problem* prob, size_t* bytes);
 /* Which kernel path iha_forward takes for this problem: IHA_PLAN_* bits written
  * to *plan (host-side only, no device work).  IHA_PLAN_MIX_FUSED: the pseudo-head
  * mixing (Algorithm 1, step 2) runs in the epilogue of the projection GEMM, so no
- * fp32 projections reach HBM and only the fp32 mixing of the first tokens is left
- * as a separate mixing kernel (bf16 with H = 16 and D a multiple of 256, or H = 20
- * and D a multiple of 320, and P in {1, 2}).  Validates the problem like
- * iha_forward does. */
+ * fp32 projections of all tokens reach HBM (only those of the first tokens, which
+ * the attention launch mixes in fp32 for the first stacked rows) and there is no
+ * separate mixing kernel (bf16 with H = 16 and D a multiple of 256, or H = 20 and
+ * D a multiple of 320, and P in {1, 2}).  Validates the problem like iha_forward
+ * does. */
 #define IHA_PLAN_MIX_FUSED 1u
 iha_status iha_plan(const iha_problem* prob, uint32_t* plan);
 
