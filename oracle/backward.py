@@ -16,8 +16,8 @@ step's definition:
 
 The loss is L = sum(G * X~) for a given upstream gradient G [B, N, D].  Pins: central
 finite differences of L (tests/test_oracle_backward.py); the forward part agrees with the
-C++ oracle's forward.  No HIP path computes gradients yet; this module is the reference a
-backward pass will be checked against.
+C++ oracle's forward.  attention_grads() is the same attention step on rows that are
+already stacked (the form the HIP attention backward takes), pinned the same way.
 """
 from __future__ import annotations
 
@@ -39,6 +39,54 @@ def _allowed(L: int, N: int, P: int, mask: int, window: int) -> np.ndarray:
     if mask == MASK_CAUSAL:
         return ki <= qi
     return (ki <= qi) & (ki > qi - window)
+
+
+def _allowed_stacked(L: int, mask: int, window: int) -> np.ndarray:
+    """[L, L] boolean on stacked positions directly (row i = position i)."""
+    i = np.arange(L)
+    qi, ki = i[:, None], i[None, :]
+    if mask == MASK_NONE:
+        return np.ones((L, L), dtype=bool)
+    if mask == MASK_CAUSAL:
+        return ki <= qi
+    return (ki <= qi) & (ki > qi - window)
+
+
+def attention_grads(Q, K, V, dO, mask: int, window: int) -> Dict[str, np.ndarray]:
+    """Masked softmax attention over already stacked rows and its gradients, in float64.
+
+    Q, K, V, dO: [B, L, H, d] with row i = stacked position i (the interleaved order of the
+    IHA page's figure 1); the mask is applied to i directly.  Scores S = Q K^T / sqrt(d),
+    A = softmax over each query's allowed keys, O = A V (textbook "Attention mechanism",
+    eq. 5.3 and 5.11).  For the loss L = sum(dO * O):
+      dV = A^T dO,  dA = dO V^T,  dS = A * (dA - rowsum(dA * A)),
+      dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d).
+    Returns {"O", "dQ", "dK", "dV", "lse"} (lse = natural log-sum-exp of each row's scores,
+    [B, H, L]).  A query with an empty allowed set raises ValueError."""
+    f = lambda a: np.asarray(a, dtype=np.float64)
+    Q, K, V, dO = f(Q), f(K), f(V), f(dO)
+    B, L, H, d = Q.shape
+    allowed = _allowed_stacked(L, mask, window)
+    if not allowed.any(axis=1).all():
+        raise ValueError("a query has an empty allowed set")
+    out = {k: np.zeros_like(Q) for k in ("O", "dQ", "dK", "dV")}
+    out["lse"] = np.zeros((B, H, L))
+    for b in range(B):
+        for h in range(H):
+            q, k, v, go = Q[b, :, h], K[b, :, h], V[b, :, h], dO[b, :, h]
+            S = np.where(allowed, q @ k.T / np.sqrt(d), -np.inf)
+            mx = S.max(axis=1, keepdims=True)
+            E = np.where(allowed, np.exp(S - mx), 0.0)
+            z = E.sum(axis=1, keepdims=True)
+            A = E / z
+            out["lse"][b, h] = (mx + np.log(z))[:, 0]
+            out["O"][b, :, h] = A @ v
+            out["dV"][b, :, h] = A.T @ go
+            dA = go @ v.T
+            dS = A * (dA - (dA * A).sum(axis=1, keepdims=True))
+            out["dQ"][b, :, h] = dS @ k / np.sqrt(d)
+            out["dK"][b, :, h] = dS.T @ q / np.sqrt(d)
+    return out
 
 
 def forward_and_grads(X, WQ, WK, WV, aQ, aK, aV, R, H: int, P: int, mask: int, window: int,
