@@ -164,6 +164,32 @@ iha_status iha_attention(int64_t B, int64_t L, int64_t H, int64_t d, int32_t mas
                          const void* Vt, float* O, uint32_t flags, void* flag_buf,
                          hipStream_t stream);
 
+/* Gradients of that attention step (the backward pass of iha_attention), by the
+ * chain rule through the scaled dot product and the row softmax (textbook eq.
+ * 5.3 and 5.11): for the upstream gradient dO of O = softmax(s) V with base-2
+ * scores s = (q_i . k_i') * score_scale over each row's visible keys,
+ *   dV = A^T dO,  dS = A * (dO V^T - rowsum(dO * O)),
+ *   dQ = dS K * score_scale * ln 2,  dK = dS^T Q * score_scale * ln 2
+ * (A: the probabilities; dS: the gradient of the natural-log scores).
+ *   Q, K, V, dO   fp16 [B][L][H][d]   (row i = stacked position i; note that V is
+ *                                     row-major here, unlike iha_attention's Vt)
+ *   dQ, dK, dV    float [B][L][H][d]
+ * All seven device pointers 16-byte aligned, else IHA_ERR_INVALID_ARG.  mask and
+ * window as above on i; d must be 64 or 128 (IHA_ERR_UNSUPPORTED), H at most 64
+ * and B at most 65535 (IHA_ERR_SHAPE), window >= 1 in window mode
+ * (IHA_ERR_EMPTY_ROW).  The forward is recomputed inside (fp16 Q * score_scale,
+ * fp16 O, fp32 per-row log-sum-exp) into `workspace`: device, 256-byte aligned,
+ * at least iha_attention_backward_workspace() bytes, else IHA_ERR_WORKSPACE.
+ * Operands of the matrix-core products are fp16 (the probabilities and dS
+ * rounded to fp16), accumulation fp32.  Enqueued on `stream`, no wait. */
+iha_status iha_attention_backward_workspace(int64_t B, int64_t L, int64_t H, int64_t d,
+                                            size_t* bytes);
+iha_status iha_attention_backward(int64_t B, int64_t L, int64_t H, int64_t d, int32_t mask,
+                                  int64_t window, float score_scale, const void* Q,
+                                  const void* K, const void* V, const void* dO, float* dQ,
+                                  float* dK, float* dV, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* iha_status_str(iha_status status);
 

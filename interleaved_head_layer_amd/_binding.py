@@ -39,6 +39,36 @@ class iha_problem(ctypes.Structure):
 _lib = None
 
 
+def iha_attention_backward(Q, K, V, dO, mask_mode, window: Optional[int] = None,
+                           score_scale: Optional[float] = None, workspace=None):
+    """Gradients of the attention step on stacked tensors: Q, K, V, dO fp16 [B, L, H, d]
+    (V row-major).  Returns (dQ, dK, dV), fp32 [B, L, H, d].  score_scale defaults to
+    log2(e)/sqrt(d)."""
+    import torch
+    B, L, H, d = (int(s) for s in Q.shape)
+    mask = _mask_code(mask_mode)
+    if window is None:
+        window = 0
+    if score_scale is None:
+        score_scale = math.log2(math.e) / math.sqrt(d)
+    ptrs = [_dev_ptr(t, n, torch.float16, (B, L, H, d)) for t, n in ((Q, "Q"), (K, "K"), (V, "V"), (dO, "dO"))]
+    lib = load_library()
+    nbytes = ctypes.c_size_t(0)
+    st = lib.iha_attention_backward_workspace(B, L, H, d, ctypes.byref(nbytes))
+    if st != IHA_OK:
+        raise IHAError(st, "iha_attention_backward_workspace")
+    if workspace is None:
+        workspace = torch.empty(max(int(nbytes.value), 1), dtype=torch.uint8, device=Q.device)
+    grads = [torch.empty((B, L, H, d), dtype=torch.float32, device=Q.device) for _ in range(3)]
+    stream = ctypes.c_void_p(torch.cuda.current_stream(Q.device).cuda_stream)
+    st = lib.iha_attention_backward(B, L, H, d, mask, int(window), float(score_scale), *ptrs,
+                                    *[ctypes.c_void_p(g.data_ptr()) for g in grads],
+                                    ctypes.c_void_p(workspace.data_ptr()), int(workspace.numel()), stream)
+    if st != IHA_OK:
+        raise IHAError(st, "iha_attention_backward")
+    return tuple(grads)
+
+
 def load_library() -> ctypes.CDLL:
     """Load libiha.so (built in-tree by __graft_entry__.build()); raise if it is missing."""
     global _lib
@@ -61,6 +91,11 @@ def load_library() -> ctypes.CDLL:
         lib.iha_attention.argtypes = [i64, i64, i64, i64, i32, i64, ctypes.c_float, vp, vp, vp, vp,
                                       u32, vp, vp]
         lib.iha_attention.restype = ctypes.c_int
+        lib.iha_attention_backward_workspace.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
+        lib.iha_attention_backward_workspace.restype = ctypes.c_int
+        lib.iha_attention_backward.argtypes = [i64, i64, i64, i64, i32, i64, ctypes.c_float, vp, vp, vp, vp,
+                                               vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.iha_attention_backward.restype = ctypes.c_int
         lib.iha_status_str.argtypes = [ctypes.c_int]
         lib.iha_status_str.restype = ctypes.c_char_p
         _lib = lib

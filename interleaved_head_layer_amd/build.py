@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJDIR = os.path.join(ROOT, "_build", "iha")
 LIB = os.path.join(PKG, "libiha.so")
-SOURCES = ["iha.hip", "fold.hip", "gemm.hip", "proj.hip", "attn.hip", "collapse.hip"]
+SOURCES = ["iha.hip", "fold.hip", "gemm.hip", "proj.hip", "attn.hip", "attn_bwd.hip", "collapse.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

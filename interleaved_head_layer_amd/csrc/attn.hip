@@ -518,6 +518,8 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
   }
 
   const float lt = st.l + __shfl_xor(st.l, 32);
+  if (a.lse && hf == 0 && qrow < L)
+    a.lse[static_cast<int64_t>(b * H + h) * L + qrow] = lt > 0.f ? st.m + __log2f(lt) : __builtin_inff();
   if (qrow < L) {
     // lt > 0 for every valid row; lt == 0 means nothing was visible (reported, output 0);
     // a NaN sum (non-finite input) is passed through to the output.

@@ -1,0 +1,387 @@
+// Gradients of masked softmax attention over stacked rows: the backward pass of the attention
+// step of the IHA forward (Algorithm 1 of the "Interleaved Head Attention" page, step 3), by
+// the chain rule through the scaled dot product and the row softmax of the textbook chapter
+// "Attention mechanism" (eq. 5.3 and 5.11).  With base-2 scores s = (q . k) * scale, the
+// probabilities A = exp2(s - lse) of each row over its visible keys, O = A V and the upstream
+// gradient dO:
+//   dV = A^T dO,   dA = dO V^T,   dS = A * (dA - D)   with D_i = sum_c dO[i][c] O[i][c]
+//   dQ = dS K * scale * ln 2,   dK = dS^T Q * scale * ln 2
+// (dS is the gradient of the natural-log scores, which are s * ln 2).  The probabilities are
+// recomputed from the forward kernel's per-row base-2 log-sum-exp.
+//
+// Two matrix-core kernels, both with fp16 operands and fp32 accumulation:
+//  * dQ: a workgroup holds 128 query rows (32 per wave, with their dO rows, in registers) and
+//    walks the key tiles their masks reach, like the forward: S^T = K Q^T and dA^T = V dO^T
+//    give one query per lane, dQ^T += K^T dS^T.  It also writes D.
+//  * dK, dV: a workgroup holds 128 keys (32 per wave, with their V rows) and walks the query
+//    tiles that see them: S = Q K^T and dA = dO V^T give one key per lane, then
+//    dV^T += dO^T A and dK^T += Q^T dS.
+// The operand that is contracted over in the second product needs the other orientation, so
+// a prep kernel writes channel-major copies of Q, K, V and dO once.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace iha {
+namespace {
+
+constexpr int BWaves = 4, BThreads = BWaves * 64;
+constexpr int QRows = 128;  // queries per dQ workgroup
+constexpr int KTile = 64;   // keys per dQ tile
+constexpr int KRows = 128;  // keys per dK/dV workgroup
+constexpr int QTile = 32;   // queries per dK/dV tile
+constexpr int Pad = 8;      // fp16 padding per LDS row (keeps 16-byte rows, spreads banks)
+
+// Rows of a 32-row MFMA A operand are loaded in this order so that lane half hf of the
+// product's output holds rows 16*hf .. 16*hf + 15 of the block in its 16 accumulators - the
+// layout the next product takes as its contracted (B operand) dimension.
+__device__ __forceinline__ int sigma(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
+
+template <int MASK>
+__device__ __forceinline__ bool seen(int q, int k, int L, int window) {
+  if (q >= L || k >= L) return false;
+  if (MASK == kMaskNone) return true;
+  return k <= q && (MASK == kMaskCausal || k > q - window);
+}
+
+// Channel-major copies [B][H][d][ld] of the row-major [B][L][H][d] inputs (ld = Lp, zero
+// padded past L, for Q*scale, K and dO; ld = L for V, which the forward kernel reads), and
+// Q*scale rounded to fp16 in row-major form.  One workgroup per (64-row tile, h, b).
+template <int DH>
+__global__ __launch_bounds__(BThreads) void bwd_prep_kernel(AttnBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) half_t tile[64][DH + Pad];
+  constexpr int CH = DH / 8;
+  const int l0 = blockIdx.x * 64, h = blockIdx.y, b = blockIdx.z;
+  const int L = a.L, H = a.H;
+  const int64_t rs = static_cast<int64_t>(H) * DH;
+  for (int t = 0; t < 4; ++t) {
+    const half_t* src = t == 0 ? a.Q : t == 1 ? a.K : t == 2 ? a.V : a.dO;
+    half_t* dst = t == 0 ? a.QsT : t == 1 ? a.KT : t == 2 ? a.VT : a.dOT;
+    const int ld = t == 2 ? L : a.Lp;
+    for (int idx = threadIdx.x; idx < 64 * CH; idx += BThreads) {
+      const int r = idx / CH, c8 = idx % CH, l = l0 + r;
+      half8 v = {};
+      if (l < L) {
+        const int64_t off = (static_cast<int64_t>(b) * L + l) * rs + h * DH + c8 * 8;
+        v = *reinterpret_cast<const half8*>(src + off);
+        if (t == 0) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = static_cast<half_t>(static_cast<float>(v[e]) * a.scale);
+          *reinterpret_cast<half8*>(a.Qs + off) = v;
+        }
+      }
+      *reinterpret_cast<half8*>(&tile[r][c8 * 8]) = v;
+    }
+    __syncthreads();
+    half_t* base = dst + static_cast<int64_t>(b * H + h) * DH * ld;
+    for (int idx = threadIdx.x; idx < DH * 8; idx += BThreads) {
+      const int c = idx % DH, u = idx / DH, l = l0 + 8 * u;
+      if (l >= ld) continue;
+      half8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = tile[8 * u + e][c];
+      half_t* p = base + static_cast<int64_t>(c) * ld + l;
+      if (t != 2 || ((L & 7) == 0 && l + 8 <= L)) {
+        *reinterpret_cast<half8*>(p) = v;
+      } else {
+        for (int e = 0; e < 8 && l + e < L; ++e) p[e] = v[e];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int DH, int MASK>
+__global__ __launch_bounds__(BThreads) void bwd_dq_kernel(AttnBwdArgs a) {
+  constexpr int NKS = DH / 16, NCB = DH / 32, RS = DH + Pad, TS = KTile + Pad;
+  __shared__ __attribute__((aligned(16))) half_t ks[KTile][RS];  // K rows of the tile
+  __shared__ __attribute__((aligned(16))) half_t vs[KTile][RS];  // V rows
+  __shared__ __attribute__((aligned(16))) half_t kt[DH][TS];     // K^T: [channel][key]
+  const int L = a.L, H = a.H, window = a.window, Lp = a.Lp;
+  const int nqt = (L + QRows - 1) / QRows;
+  const int bh = blockIdx.x / nqt, qt = blockIdx.x % nqt;
+  const int b = bh / H, h = bh % H, q0 = qt * QRows;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int64_t rs = static_cast<int64_t>(H) * DH;
+  const int64_t rbase = static_cast<int64_t>(b) * L * rs + h * DH;  // row-major tensors
+  const int64_t tbase = static_cast<int64_t>(b * H + h) * DH * Lp;  // channel-major, padded
+  const int64_t sbase = static_cast<int64_t>(b * H + h) * L;        // lse, D
+  const int r0 = q0 + 32 * w, qrow = r0 + l32, qload = min(qrow, L - 1);
+
+  // This lane's row: Q*scale and dO fragments (B operands), and D = dO . O over the row (the
+  // two lane halves hold the two halves of each 16-channel step).
+  half8 qf[NKS], gf[NKS];
+  float dd = 0.f;
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    const int64_t off = rbase + static_cast<int64_t>(qload) * rs + (2 * s + hf) * 8;
+    qf[s] = *reinterpret_cast<const half8*>(a.Qs + off);
+    gf[s] = *reinterpret_cast<const half8*>(a.dO + off);
+    const half8 of = *reinterpret_cast<const half8*>(a.O + off);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dd = fmaf(static_cast<float>(gf[s][e]), static_cast<float>(of[e]), dd);
+  }
+  dd += __shfl_xor(dd, 32);
+  const float lse = qrow < L ? a.lse[sbase + qrow] : __builtin_inff();
+  if (hf == 0 && qrow < L) a.D[sbase + qrow] = dd;
+
+  floatx16 acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+
+  int klo = 0, khi = L;
+  if (MASK != kMaskNone) khi = min(L, q0 + QRows);
+  if (MASK == kMaskWindow) klo = max(0, q0 - window + 1);
+  const int kt0 = klo / KTile, kt1 = (khi + KTile - 1) / KTile;
+  for (int kti = kt0; kti < kt1; ++kti) {
+    const int k0 = kti * KTile;
+    __syncthreads();  // the previous tile is no longer read
+    for (int idx = tid; idx < KTile * (DH / 8); idx += BThreads) {
+      const int r = idx / (DH / 8), c8 = idx % (DH / 8), key = k0 + r;
+      half8 kv = {}, vv = {};
+      if (key < L) {
+        const int64_t off = rbase + static_cast<int64_t>(key) * rs + c8 * 8;
+        kv = *reinterpret_cast<const half8*>(a.K + off);
+        vv = *reinterpret_cast<const half8*>(a.V + off);
+      }
+      *reinterpret_cast<half8*>(&ks[r][c8 * 8]) = kv;
+      *reinterpret_cast<half8*>(&vs[r][c8 * 8]) = vv;
+    }
+    for (int idx = tid; idx < DH * (KTile / 8); idx += BThreads) {
+      const int c = idx / (KTile / 8), u = idx % (KTile / 8);
+      *reinterpret_cast<half8*>(&kt[c][u * 8]) =
+          *reinterpret_cast<const half8*>(a.KT + tbase + static_cast<int64_t>(c) * Lp + k0 + u * 8);
+    }
+    __syncthreads();
+    // Tiles with no visible key for the wave's rows are skipped; only tiles that cross a mask
+    // edge or the end of the sequence test each pair.
+    bool act = true, edge = k0 + KTile > L || r0 + 32 > L;
+    if (MASK != kMaskNone) {
+      act = k0 <= r0 + 31;
+      edge |= k0 + KTile - 1 > r0;
+    }
+    if (MASK == kMaskWindow) {
+      act = act && (k0 + KTile - 1 > r0 - window);
+      edge |= k0 <= r0 + 31 - window;
+    }
+    if (!act) continue;
+    floatx16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
+#pragma unroll
+      for (int st = 0; st < NKS; ++st) {
+        const int kr = kb * 32 + sigma(l32), col = (2 * st + hf) * 8;
+        s[kb] = mfma32(*reinterpret_cast<const half8*>(&ks[kr][col]), qf[st], s[kb]);
+        dp[kb] = mfma32(*reinterpret_cast<const half8*>(&vs[kr][col]), gf[st], dp[kb]);
+      }
+    }
+    // Lane (l32, hf), accumulator r of block kb: query qrow, key k0 + 32*kb + 16*hf + r.
+    half8 dsf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(s[kb][r] - lse);
+        if (edge && !seen<MASK>(qrow, k0 + kb * 32 + 16 * hf + r, L, window)) p = 0.f;
+        dsf[kb][r >> 3][r & 7] = static_cast<half_t>(p * (dp[kb][r] - dd));
+      }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+          acc[cb] = mfma32(*reinterpret_cast<const half8*>(&kt[cb * 32 + l32][kb * 32 + 16 * hf + 8 * s2]),
+                           dsf[kb][s2], acc[cb]);
+  }
+  // acc[cb] accumulator r: channel cb*32 + 8*(r/4) + 4*hf + r%4 of query qrow.
+  if (qrow < L) {
+    float* dst = a.dQ + rbase + static_cast<int64_t>(qrow) * rs;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        floatx4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[cb][4 * q4 + e] * a.dq_scale;
+        *reinterpret_cast<floatx4*>(dst + cb * 32 + 8 * q4 + 4 * hf) = v;
+      }
+  }
+}
+
+template <int DH, int MASK>
+__global__ __launch_bounds__(BThreads) void bwd_dkdv_kernel(AttnBwdArgs a) {
+  constexpr int NKS = DH / 16, NCB = DH / 32, RS = DH + Pad, TS = QTile + Pad;
+  __shared__ __attribute__((aligned(16))) half_t qs[QTile][RS];  // Q*scale rows of the tile
+  __shared__ __attribute__((aligned(16))) half_t gs[QTile][RS];  // dO rows
+  __shared__ __attribute__((aligned(16))) half_t qt[DH][TS];     // (Q*scale)^T: [channel][query]
+  __shared__ __attribute__((aligned(16))) half_t gt[DH][TS];     // dO^T
+  __shared__ __attribute__((aligned(16))) float ls[QTile], ds[QTile];
+  const int L = a.L, H = a.H, window = a.window, Lp = a.Lp;
+  const int nkt = (L + KRows - 1) / KRows;
+  const int bh = blockIdx.x / nkt, kti = blockIdx.x % nkt;
+  const int b = bh / H, h = bh % H, k0 = kti * KRows;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int64_t rs = static_cast<int64_t>(H) * DH;
+  const int64_t rbase = static_cast<int64_t>(b) * L * rs + h * DH;
+  const int64_t tbase = static_cast<int64_t>(b * H + h) * DH * Lp;
+  const int64_t sbase = static_cast<int64_t>(b * H + h) * L;
+  const int kw0 = k0 + 32 * w, krow = kw0 + l32, kload = min(krow, L - 1);
+
+  half8 kf[NKS], vf[NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    const int64_t off = rbase + static_cast<int64_t>(kload) * rs + (2 * s + hf) * 8;
+    kf[s] = *reinterpret_cast<const half8*>(a.K + off);
+    vf[s] = *reinterpret_cast<const half8*>(a.V + off);
+  }
+  floatx16 dv[NCB], dk[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dv[cb][r] = dk[cb][r] = 0.f;
+
+  // Queries that see a key of [k0, k0 + KRows): causal q >= k0, window also q < key + window.
+  int qlo = 0, qhi = L;
+  if (MASK != kMaskNone) qlo = k0;
+  if (MASK == kMaskWindow) qhi = min(L, k0 + KRows - 1 + window);
+  const int qt0 = qlo / QTile, qt1 = (qhi + QTile - 1) / QTile;
+  for (int qti = qt0; qti < qt1; ++qti) {
+    const int q0 = qti * QTile;
+    __syncthreads();
+    for (int idx = tid; idx < QTile * (DH / 8); idx += BThreads) {
+      const int r = idx / (DH / 8), c8 = idx % (DH / 8), q = q0 + r;
+      half8 qv = {}, gv = {};
+      if (q < L) {
+        const int64_t off = rbase + static_cast<int64_t>(q) * rs + c8 * 8;
+        qv = *reinterpret_cast<const half8*>(a.Qs + off);
+        gv = *reinterpret_cast<const half8*>(a.dO + off);
+      }
+      *reinterpret_cast<half8*>(&qs[r][c8 * 8]) = qv;
+      *reinterpret_cast<half8*>(&gs[r][c8 * 8]) = gv;
+    }
+    for (int idx = tid; idx < DH * (QTile / 8); idx += BThreads) {
+      const int c = idx / (QTile / 8), u = idx % (QTile / 8);
+      const int64_t off = tbase + static_cast<int64_t>(c) * Lp + q0 + u * 8;
+      *reinterpret_cast<half8*>(&qt[c][u * 8]) = *reinterpret_cast<const half8*>(a.QsT + off);
+      *reinterpret_cast<half8*>(&gt[c][u * 8]) = *reinterpret_cast<const half8*>(a.dOT + off);
+    }
+    if (tid < QTile) {
+      const int q = q0 + tid;
+      ls[tid] = q < L ? a.lse[sbase + q] : __builtin_inff();
+      ds[tid] = q < L ? a.D[sbase + q] : 0.f;
+    }
+    __syncthreads();
+    // Visible pairs in (query tile) x (the wave's 32 keys): causal needs kw0 <= q0 + 31,
+    // window also q0 < kw0 + 31 + window.
+    bool act = true, edge = q0 + QTile > L || kw0 + 32 > L;
+    if (MASK != kMaskNone) {
+      act = kw0 <= q0 + QTile - 1;
+      edge |= kw0 + 31 > q0;
+    }
+    if (MASK == kMaskWindow) {
+      act = act && (q0 < kw0 + 31 + window);
+      edge |= q0 + QTile - 1 >= kw0 + window;
+    }
+    if (!act) continue;
+    floatx16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+    for (int st = 0; st < NKS; ++st) {
+      const int qr = sigma(l32), col = (2 * st + hf) * 8;
+      s = mfma32(*reinterpret_cast<const half8*>(&qs[qr][col]), kf[st], s);
+      dp = mfma32(*reinterpret_cast<const half8*>(&gs[qr][col]), vf[st], dp);
+    }
+    // Lane (l32, hf), accumulator r: key krow, query q0 + 16*hf + r.
+    half8 pf[2], sf[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qi = 16 * hf + r;
+      float p = fast_exp2(s[r] - ls[qi]);
+      if (edge && !seen<MASK>(q0 + qi, krow, L, window)) p = 0.f;
+      pf[r >> 3][r & 7] = static_cast<half_t>(p);
+      sf[r >> 3][r & 7] = static_cast<half_t>(p * (dp[r] - ds[qi]));
+    }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int c = cb * 32 + l32, col = 16 * hf + 8 * s2;
+        dv[cb] = mfma32(*reinterpret_cast<const half8*>(&gt[c][col]), pf[s2], dv[cb]);
+        dk[cb] = mfma32(*reinterpret_cast<const half8*>(&qt[c][col]), sf[s2], dk[cb]);
+      }
+  }
+  // dv[cb], dk[cb] accumulator r: channel cb*32 + 8*(r/4) + 4*hf + r%4 of key krow.
+  if (krow < L) {
+    const int64_t off = rbase + static_cast<int64_t>(krow) * rs;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        floatx4 v, k;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = dv[cb][4 * q4 + e];
+          k[e] = dk[cb][4 * q4 + e] * a.dk_scale;
+        }
+        *reinterpret_cast<floatx4*>(a.dV + off + cb * 32 + 8 * q4 + 4 * hf) = v;
+        *reinterpret_cast<floatx4*>(a.dK + off + cb * 32 + 8 * q4 + 4 * hf) = k;
+      }
+  }
+}
+
+template <int DH, int MASK>
+hipError_t launch_grads(const AttnBwdArgs& a, hipStream_t s) {
+  const int nqt = (a.L + QRows - 1) / QRows, nkt = (a.L + KRows - 1) / KRows;
+  hipLaunchKernelGGL((bwd_dq_kernel<DH, MASK>), dim3(nqt * a.H * a.B), dim3(BThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<DH, MASK>), dim3(nkt * a.H * a.B), dim3(BThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DH>
+hipError_t launch_bwd_d(const AttnBwdArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_prep_kernel<DH>), dim3(a.Lp / 64, a.H, a.B), dim3(BThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // Forward recompute: O (fp16) and the per-row log-sum-exp, from the scaled Q.
+  AttnArgs f{};
+  f.Q = a.Qs;
+  f.K = a.K;
+  f.Vt = a.VT;
+  f.Oh = a.O;
+  f.B = a.B;
+  f.L = a.L;
+  f.H = a.H;
+  f.d = DH;
+  f.mask = a.mask;
+  f.window = a.window;
+  f.qk_scale = 1.f;
+  f.qk_layout = kQKRowMajor;
+  f.lse = a.lse;
+  e = launch_attn_f16(f, s);
+  if (e != hipSuccess) return e;
+  switch (a.mask) {
+    case kMaskNone: return launch_grads<DH, kMaskNone>(a, s);
+    case kMaskCausal: return launch_grads<DH, kMaskCausal>(a, s);
+    default: return launch_grads<DH, kMaskWindow>(a, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s) {
+  if (a.Lp % 64 != 0 || a.Lp < a.L) return hipErrorInvalidValue;
+  switch (a.d) {
+    case 64: return launch_bwd_d<64>(a, s);
+    case 128: return launch_bwd_d<128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace iha

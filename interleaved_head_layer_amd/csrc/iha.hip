@@ -292,6 +292,44 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
   return IHA_OK;
 }
 
+// Workspace of iha_attention_backward: fp16 Q*scale, channel-major copies (Q*scale, K and dO
+// with rows padded to Lp, V with L), the recomputed fp16 forward output, and fp32 lse and D.
+struct BwdLayout {
+  size_t qs, qst, kt, dot, vt, o, lse, dd, total;
+  int64_t Lp;
+};
+
+BwdLayout bwd_layout(int64_t B, int64_t L, int64_t H, int64_t d) {
+  BwdLayout l{};
+  l.Lp = (L + 63) / 64 * 64;
+  const size_t E = static_cast<size_t>(B * L * H * d), Et = static_cast<size_t>(B * H * d * l.Lp);
+  const size_t S = static_cast<size_t>(B * H * L);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  l.qs = take(E * 2);
+  l.qst = take(Et * 2);
+  l.kt = take(Et * 2);
+  l.dot = take(Et * 2);
+  l.vt = take(E * 2);
+  l.o = take(E * 2);
+  l.lse = take(S * 4);
+  l.dd = take(S * 4);
+  l.total = off;
+  return l;
+}
+
+iha_status bwd_validate(int64_t B, int64_t L, int64_t H, int64_t d, int32_t mask, int64_t window) {
+  if (B < 1 || L < 1 || H < 1 || mask < IHA_MASK_NONE || mask > IHA_MASK_WINDOW) return IHA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return IHA_ERR_UNSUPPORTED;
+  if (H > kMaxH || B > 65535 || L > kMaxRows || B * (L + 63) * H * d > kMaxElems / 4) return IHA_ERR_SHAPE;
+  if (mask == IHA_MASK_WINDOW && window < 1) return IHA_ERR_EMPTY_ROW;
+  return IHA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -362,6 +400,59 @@ iha_status iha_attention(int64_t B, int64_t L, int64_t H, int64_t d, int32_t mas
   at.qk_scale = score_scale;
   IHA_HIP(iha::launch_attn_f16(at, stream));
   if (flags & IHA_FLAG_CHECK) return read_flag(flag, stream);
+  return IHA_OK;
+}
+
+iha_status iha_attention_backward_workspace(int64_t B, int64_t L, int64_t H, int64_t d, size_t* bytes) {
+  if (!bytes) return IHA_ERR_INVALID_ARG;
+  const iha_status st = bwd_validate(B, L, H, d, IHA_MASK_NONE, 0);
+  if (st != IHA_OK) return st;
+  *bytes = bwd_layout(B, L, H, d).total;
+  return IHA_OK;
+}
+
+iha_status iha_attention_backward(int64_t B, int64_t L, int64_t H, int64_t d, int32_t mask, int64_t window,
+                                  float score_scale, const void* Q, const void* K, const void* V,
+                                  const void* dO, float* dQ, float* dK, float* dV, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  const iha_status st = bwd_validate(B, L, H, d, mask, window);
+  if (st != IHA_OK) return st;
+  if (!Q || !K || !V || !dO || !dQ || !dK || !dV || !(score_scale > 0.f) || !std::isfinite(score_scale))
+    return IHA_ERR_INVALID_ARG;
+  for (const void* p : {Q, K, V, dO, static_cast<const void*>(dQ), static_cast<const void*>(dK),
+                        static_cast<const void*>(dV)})
+    if (!aligned(p, 16)) return IHA_ERR_INVALID_ARG;
+  const BwdLayout lay = bwd_layout(B, L, H, d);
+  if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < lay.total) return IHA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  iha::AttnBwdArgs a{};
+  using iha::half_t;
+  a.Q = static_cast<const half_t*>(Q);
+  a.K = static_cast<const half_t*>(K);
+  a.V = static_cast<const half_t*>(V);
+  a.dO = static_cast<const half_t*>(dO);
+  a.dQ = dQ;
+  a.dK = dK;
+  a.dV = dV;
+  a.Qs = reinterpret_cast<half_t*>(ws + lay.qs);
+  a.QsT = reinterpret_cast<half_t*>(ws + lay.qst);
+  a.KT = reinterpret_cast<half_t*>(ws + lay.kt);
+  a.dOT = reinterpret_cast<half_t*>(ws + lay.dot);
+  a.VT = reinterpret_cast<half_t*>(ws + lay.vt);
+  a.O = reinterpret_cast<half_t*>(ws + lay.o);
+  a.lse = reinterpret_cast<float*>(ws + lay.lse);
+  a.D = reinterpret_cast<float*>(ws + lay.dd);
+  a.B = static_cast<int>(B);
+  a.L = static_cast<int>(L);
+  a.H = static_cast<int>(H);
+  a.d = static_cast<int>(d);
+  a.mask = mask;
+  a.window = mask == IHA_MASK_WINDOW ? static_cast<int>(window < L ? window : L) : 0;
+  a.Lp = static_cast<int>(lay.Lp);
+  a.scale = score_scale;
+  a.dq_scale = score_scale * 0.69314718055994531f;
+  a.dk_scale = 0.69314718055994531f;
+  IHA_HIP(iha::launch_attn_bwd(a, stream));
   return IHA_OK;
 }
 

@@ -66,8 +66,39 @@ struct AttnArgs {
   float* Pe;
   int R, P, T0;
   float escale;
+  // fp16 kernel: when set, [B][H][L] base-2 log-sum-exp of every row's visible scores
+  // (the row's probabilities are exp2(score - lse)); +inf for a row with no visible key.
+  float* lse;
 };
 hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s);
+
+// Attention backward over stacked rows (fp16 operands, fp32 gradients).  Inputs Q, K, V, dO
+// and outputs dQ, dK, dV are row-major [B][L][H][d]; the rest is workspace the launcher fills:
+// Qs = fp16(Q * scale) [B][L][H][d], channel-major QsT, KT, dOT [B][H][d][Lp] (Lp: L rounded
+// up to 64, zero padded) and VT [B][H][d][L], the recomputed forward output O (fp16,
+// [B][L][H][d]), and per-row lse (base 2) and D = dO . O, [B][H][L] fp32.
+struct AttnBwdArgs {
+  const half_t* Q;
+  const half_t* K;
+  const half_t* V;
+  const half_t* dO;
+  float* dQ;
+  float* dK;
+  float* dV;
+  half_t* Qs;
+  half_t* QsT;
+  half_t* KT;
+  half_t* dOT;
+  half_t* VT;
+  half_t* O;
+  float* lse;
+  float* D;
+  int B, L, H, d, mask, window, Lp;
+  float scale;     // base-2 score scale
+  float dq_scale;  // scale * ln 2
+  float dk_scale;  // ln 2 (dK is formed from the scaled Q)
+};
+hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
 
 // bf16 projection path: exact bf16 GEMMs (fp32 accumulation) then fp32 mixing.

@@ -177,6 +177,13 @@ def make_stacked_qkv(B: int, PN: int, H: int, d: int, seed: int, scale: float = 
     return q.astype(np.float32), k.astype(np.float32), v.astype(np.float32)
 
 
+def make_stacked_grad(B: int, PN: int, H: int, d: int, seed: int) -> np.ndarray:
+    """Draw an fp16-representable upstream gradient dO of shape [B, PN, H, d], N(0, 1) before
+    rounding (float32 holding fp16 numbers), for the attention backward."""
+    rng = np.random.Generator(np.random.PCG64([seed, 99]))
+    return rng.standard_normal((B, PN, H, d), dtype=np.float32).astype(np.float16).astype(np.float32)
+
+
 def sample_tokens(w: Workload, n: int, seed: int = 0) -> np.ndarray:
     """Flat token indices b*N + t to check at full size: the first and last tokens of each
     sequence (fewest / most visible keys) plus uniformly drawn ones, sorted and unique."""

@@ -23,7 +23,8 @@ def test_library_loads_and_exports_every_declared_symbol():
     lib = bd.load_library()
     names = declared_functions()
     assert {"iha_forward", "iha_workspace_bytes", "iha_status_str", "iha_attention",
-            "iha_forward_timed", "iha_plan"} <= set(names)
+            "iha_forward_timed", "iha_plan", "iha_attention_backward",
+            "iha_attention_backward_workspace"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -153,3 +154,28 @@ def test_timed_event_count_matches_header():
     hdr = open(os.path.join(ROOT, "include", "iha.h")).read()
     m = re.search(r"#define\s+IHA_TIMED_EVENTS\s+(\d+)", hdr)
     assert m and int(m.group(1)) == bd.TIMED_EVENTS
+
+
+def test_attention_backward_workspace_and_validation():
+    """Host-side only: the workspace formula (fp16 Q*scale, three padded channel-major copies,
+    V^T, the fp16 forward output, fp32 lse and D) and the argument checks, which return before
+    any launch."""
+    lib = bd.load_library()
+    n = ctypes.c_size_t(0)
+    B, L, H, d = 2, 300, 3, 64
+    assert lib.iha_attention_backward_workspace(B, L, H, d, ctypes.byref(n)) == 0
+    up = lambda x: (x + 255) // 256 * 256
+    E, Et, S = B * L * H * d, B * H * d * 320, B * H * L
+    assert n.value == 3 * up(E * 2) + 3 * up(Et * 2) + 2 * up(S * 4)
+    assert lib.iha_attention_backward_workspace(B, L, H, 96, ctypes.byref(n)) == bd.STATUS_NAMES.index("IHA_ERR_UNSUPPORTED")
+    assert lib.iha_attention_backward_workspace(B, L, 65, d, ctypes.byref(n)) == bd.STATUS_NAMES.index("IHA_ERR_SHAPE")
+    assert lib.iha_attention_backward_workspace(0, L, H, d, ctypes.byref(n)) == bd.STATUS_NAMES.index("IHA_ERR_INVALID_ARG")
+    fake = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 8)
+    args = lambda mask, window, scale, qp=fake, ws=fake, nb=1 << 40: (
+        B, L, H, d, mask, window, scale, qp, fake, fake, fake, fake, fake, fake, ws, nb, None)
+    assert lib.iha_attention_backward(*args(2, 0, 1.0)) == bd.STATUS_NAMES.index("IHA_ERR_EMPTY_ROW")
+    assert lib.iha_attention_backward(*args(0, 0, -1.0)) == bd.STATUS_NAMES.index("IHA_ERR_INVALID_ARG")
+    assert lib.iha_attention_backward(*args(0, 0, 1.0, qp=odd)) == bd.STATUS_NAMES.index("IHA_ERR_INVALID_ARG")
+    assert lib.iha_attention_backward(*args(1, 0, 1.0, ws=odd)) == bd.STATUS_NAMES.index("IHA_ERR_WORKSPACE")
+    assert lib.iha_attention_backward(*args(1, 0, 1.0, nb=16)) == bd.STATUS_NAMES.index("IHA_ERR_WORKSPACE")
