@@ -24,6 +24,7 @@ Work per unit (algorithmic, the count the pages' convention gives):
   prep       bytes: 3*D^2*2 read + 3*D^2*2 written (bf16 weight transpose)
 """
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -155,6 +156,42 @@ def run_workload(w, steps, warmup):
                "roofs": roofs, "mix_fused": fused}
 
 
+def run_attention_backward(w, steps, warmup):
+    """Time iha_attention_backward on the stacked attention of workload `w` (L = P*N rows per
+    sequence, its heads, head width, mask and window), inputs resident on the GPU.  Work is
+    counted as 2.5x the forward's 4*d*(visible pairs) per head: the gradient products dV, dP,
+    dQ and dK plus the recomputed scores, 2*d flops per visible pair each."""
+    import torch
+    import interleaved_head_layer_amd as iha
+
+    B, H, d, L = w.B, w.H, w.D // w.H, w.P * w.N
+    mask = ["none", "causal", "window"][w.mask]
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    q, k, v, go = (torch.randn((B, L, H, d), generator=g, device=dev).half() for _ in range(4))
+    nbytes = ctypes.c_size_t(0)
+    lib = iha.load_library()
+    assert lib.iha_attention_backward_workspace(B, L, H, d, ctypes.byref(nbytes)) == 0
+    ws = torch.empty(int(nbytes.value), dtype=torch.uint8, device=dev)
+    call = lambda: iha.iha_attention_backward(q, k, v, go, mask, w.window, workspace=ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    work = 2.5 * 4.0 * d * B * H * allowed_pairs(L, w.mask, w.window)
+    return {"shape": {"B": B, "L": L, "H": H, "d": d, "mask": mask, "window": w.window},
+            "ms": round(ms, 4), "steps": steps, "work_flop": work,
+            "roofline": roof("mfma", work, ms),
+            "note": "whole call: prep copies, forward recompute (O, lse), dQ and dK/dV kernels"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +206,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other headline workloads")
     ap.add_argument("--extra-steps", type=int, default=5)
+    ap.add_argument("--only-backward", action="store_true",
+                    help="time only the attention backward of the workload's attention shape")
     ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (reference for HBM counters)")
     args = ap.parse_args()
@@ -190,6 +229,11 @@ def main():
         del src, dst
 
     w = wl.WORKLOADS[args.workload]
+    if args.only_backward:
+        print(json.dumps({"workload": w.name,
+                          "attention_backward": run_attention_backward(w, args.steps, args.warmup)}),
+              flush=True)
+        return
     x, r = run_workload(w, args.steps, args.warmup)
     kms, roofs = r["kms"], r["roofs"]
     dominant = max(roofs, key=lambda k: kms[k])
@@ -216,7 +260,9 @@ def main():
     del x
 
     extra = {}
+    bwd = None
     if not args.no_extra:
+        bwd = run_attention_backward(w, args.extra_steps, 3)
         for name in wl.HEADLINE + ["mha_causal_bf16"]:   # + the P = 1 MHA configuration
             if name == w.name:
                 continue
@@ -247,6 +293,7 @@ def main():
         "kernel_roofline": roofs,
         "mix_fused": r["mix_fused"],
         "other_workloads": extra,
+        "attention_backward": bwd,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -93,9 +93,12 @@ __global__ __launch_bounds__(BThreads) void bwd_prep_kernel(AttnBwdArgs a) {
 template <int DH, int MASK>
 __global__ __launch_bounds__(BThreads) void bwd_dq_kernel(AttnBwdArgs a) {
   constexpr int NKS = DH / 16, NCB = DH / 32, RS = DH + Pad, TS = KTile + Pad;
-  __shared__ __attribute__((aligned(16))) half_t ks[KTile][RS];  // K rows of the tile
-  __shared__ __attribute__((aligned(16))) half_t vs[KTile][RS];  // V rows
-  __shared__ __attribute__((aligned(16))) half_t kt[DH][TS];     // K^T: [channel][key]
+  // Two stages: the next tile's loads are held in registers during this tile's products.
+  __shared__ __attribute__((aligned(16))) half_t ks[2][KTile][RS];  // K rows of the tile
+  __shared__ __attribute__((aligned(16))) half_t vs[2][KTile][RS];  // V rows
+  __shared__ __attribute__((aligned(16))) half_t kt[2][DH][TS];     // K^T: [channel][key]
+  constexpr int NR = KTile * (DH / 8) / BThreads, NT = DH * (KTile / 8) / BThreads;
+  static_assert(NR * BThreads == KTile * (DH / 8) && NT * BThreads == DH * (KTile / 8), "tile split");
   const int L = a.L, H = a.H, window = a.window, Lp = a.Lp;
   const int nqt = (L + QRows - 1) / QRows;
   const int bh = blockIdx.x / nqt, qt = blockIdx.x % nqt;
@@ -134,26 +137,46 @@ __global__ __launch_bounds__(BThreads) void bwd_dq_kernel(AttnBwdArgs a) {
   if (MASK != kMaskNone) khi = min(L, q0 + QRows);
   if (MASK == kMaskWindow) klo = max(0, q0 - window + 1);
   const int kt0 = klo / KTile, kt1 = (khi + KTile - 1) / KTile;
-  for (int kti = kt0; kti < kt1; ++kti) {
-    const int k0 = kti * KTile;
-    __syncthreads();  // the previous tile is no longer read
-    for (int idx = tid; idx < KTile * (DH / 8); idx += BThreads) {
-      const int r = idx / (DH / 8), c8 = idx % (DH / 8), key = k0 + r;
-      half8 kv = {}, vv = {};
+  half8 pk[NR], pv[NR], pt[NT];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int idx = tid + i * BThreads, r = idx / (DH / 8), c8 = idx % (DH / 8), key = k0 + r;
+      pk[i] = pv[i] = half8{};
       if (key < L) {
         const int64_t off = rbase + static_cast<int64_t>(key) * rs + c8 * 8;
-        kv = *reinterpret_cast<const half8*>(a.K + off);
-        vv = *reinterpret_cast<const half8*>(a.V + off);
+        pk[i] = *reinterpret_cast<const half8*>(a.K + off);
+        pv[i] = *reinterpret_cast<const half8*>(a.V + off);
       }
-      *reinterpret_cast<half8*>(&ks[r][c8 * 8]) = kv;
-      *reinterpret_cast<half8*>(&vs[r][c8 * 8]) = vv;
     }
-    for (int idx = tid; idx < DH * (KTile / 8); idx += BThreads) {
-      const int c = idx / (KTile / 8), u = idx % (KTile / 8);
-      *reinterpret_cast<half8*>(&kt[c][u * 8]) =
-          *reinterpret_cast<const half8*>(a.KT + tbase + static_cast<int64_t>(c) * Lp + k0 + u * 8);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int idx = tid + i * BThreads, c = idx / (KTile / 8), u = idx % (KTile / 8);
+      pt[i] = *reinterpret_cast<const half8*>(a.KT + tbase + static_cast<int64_t>(c) * Lp + k0 + u * 8);
     }
-    __syncthreads();
+  };
+  auto store = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int idx = tid + i * BThreads, r = idx / (DH / 8), c8 = idx % (DH / 8);
+      *reinterpret_cast<half8*>(&ks[st][r][c8 * 8]) = pk[i];
+      *reinterpret_cast<half8*>(&vs[st][r][c8 * 8]) = pv[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int idx = tid + i * BThreads, c = idx / (KTile / 8), u = idx % (KTile / 8);
+      *reinterpret_cast<half8*>(&kt[st][c][u * 8]) = pt[i];
+    }
+  };
+  if (kt0 < kt1) {
+    load(kt0 * KTile);
+    store(0);
+  }
+  __syncthreads();
+  for (int kti = kt0; kti < kt1; ++kti) {
+    const int k0 = kti * KTile, stg = (kti - kt0) & 1;
+    const bool more = kti + 1 < kt1;
+    if (more) load(k0 + KTile);
     // Tiles with no visible key for the wave's rows are skipped; only tiles that cross a mask
     // edge or the end of the sequence test each pair.
     bool act = true, edge = k0 + KTile > L || r0 + 32 > L;
@@ -165,7 +188,7 @@ __global__ __launch_bounds__(BThreads) void bwd_dq_kernel(AttnBwdArgs a) {
       act = act && (k0 + KTile - 1 > r0 - window);
       edge |= k0 <= r0 + 31 - window;
     }
-    if (!act) continue;
+    if (act) {
     floatx16 s[2], dp[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -174,8 +197,8 @@ __global__ __launch_bounds__(BThreads) void bwd_dq_kernel(AttnBwdArgs a) {
 #pragma unroll
       for (int st = 0; st < NKS; ++st) {
         const int kr = kb * 32 + sigma(l32), col = (2 * st + hf) * 8;
-        s[kb] = mfma32(*reinterpret_cast<const half8*>(&ks[kr][col]), qf[st], s[kb]);
-        dp[kb] = mfma32(*reinterpret_cast<const half8*>(&vs[kr][col]), gf[st], dp[kb]);
+        s[kb] = mfma32(*reinterpret_cast<const half8*>(&ks[stg][kr][col]), qf[st], s[kb]);
+        dp[kb] = mfma32(*reinterpret_cast<const half8*>(&vs[stg][kr][col]), gf[st], dp[kb]);
       }
     }
     // Lane (l32, hf), accumulator r of block kb: query qrow, key k0 + 32*kb + 16*hf + r.
@@ -194,8 +217,12 @@ __global__ __launch_bounds__(BThreads) void bwd_dq_kernel(AttnBwdArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
-          acc[cb] = mfma32(*reinterpret_cast<const half8*>(&kt[cb * 32 + l32][kb * 32 + 16 * hf + 8 * s2]),
+          acc[cb] = mfma32(*reinterpret_cast<const half8*>(&kt[stg][cb * 32 + l32][kb * 32 + 16 * hf + 8 * s2]),
                            dsf[kb][s2], acc[cb]);
+    }
+    // The other stage was last read before the previous barrier.
+    if (more) store(stg ^ 1);
+    __syncthreads();
   }
   // acc[cb] accumulator r: channel cb*32 + 8*(r/4) + 4*hf + r%4 of query qrow.
   if (qrow < L) {
@@ -215,11 +242,13 @@ __global__ __launch_bounds__(BThreads) void bwd_dq_kernel(AttnBwdArgs a) {
 template <int DH, int MASK>
 __global__ __launch_bounds__(BThreads) void bwd_dkdv_kernel(AttnBwdArgs a) {
   constexpr int NKS = DH / 16, NCB = DH / 32, RS = DH + Pad, TS = QTile + Pad;
-  __shared__ __attribute__((aligned(16))) half_t qs[QTile][RS];  // Q*scale rows of the tile
-  __shared__ __attribute__((aligned(16))) half_t gs[QTile][RS];  // dO rows
-  __shared__ __attribute__((aligned(16))) half_t qt[DH][TS];     // (Q*scale)^T: [channel][query]
-  __shared__ __attribute__((aligned(16))) half_t gt[DH][TS];     // dO^T
-  __shared__ __attribute__((aligned(16))) float ls[QTile], ds[QTile];
+  __shared__ __attribute__((aligned(16))) half_t qs[2][QTile][RS];  // Q*scale rows of the tile
+  __shared__ __attribute__((aligned(16))) half_t gs[2][QTile][RS];  // dO rows
+  __shared__ __attribute__((aligned(16))) half_t qt[2][DH][TS];     // (Q*scale)^T: [channel][query]
+  __shared__ __attribute__((aligned(16))) half_t gt[2][DH][TS];     // dO^T
+  __shared__ __attribute__((aligned(16))) float ls[2][QTile], ds[2][QTile];
+  constexpr int NR = QTile * (DH / 8) / BThreads, NT = DH * (QTile / 8) / BThreads;
+  static_assert(NR * BThreads == QTile * (DH / 8) && NT * BThreads == DH * (QTile / 8), "tile split");
   const int L = a.L, H = a.H, window = a.window, Lp = a.Lp;
   const int nkt = (L + KRows - 1) / KRows;
   const int bh = blockIdx.x / nkt, kti = blockIdx.x % nkt;
@@ -249,32 +278,59 @@ __global__ __launch_bounds__(BThreads) void bwd_dkdv_kernel(AttnBwdArgs a) {
   if (MASK != kMaskNone) qlo = k0;
   if (MASK == kMaskWindow) qhi = min(L, k0 + KRows - 1 + window);
   const int qt0 = qlo / QTile, qt1 = (qhi + QTile - 1) / QTile;
-  for (int qti = qt0; qti < qt1; ++qti) {
-    const int q0 = qti * QTile;
-    __syncthreads();
-    for (int idx = tid; idx < QTile * (DH / 8); idx += BThreads) {
-      const int r = idx / (DH / 8), c8 = idx % (DH / 8), q = q0 + r;
-      half8 qv = {}, gv = {};
+  half8 pq[NR], pg[NR], pqt[NT], pgt[NT];
+  float pl = 0.f, pd = 0.f;
+  auto load = [&](int q0) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int idx = tid + i * BThreads, r = idx / (DH / 8), c8 = idx % (DH / 8), q = q0 + r;
+      pq[i] = pg[i] = half8{};
       if (q < L) {
         const int64_t off = rbase + static_cast<int64_t>(q) * rs + c8 * 8;
-        qv = *reinterpret_cast<const half8*>(a.Qs + off);
-        gv = *reinterpret_cast<const half8*>(a.dO + off);
+        pq[i] = *reinterpret_cast<const half8*>(a.Qs + off);
+        pg[i] = *reinterpret_cast<const half8*>(a.dO + off);
       }
-      *reinterpret_cast<half8*>(&qs[r][c8 * 8]) = qv;
-      *reinterpret_cast<half8*>(&gs[r][c8 * 8]) = gv;
     }
-    for (int idx = tid; idx < DH * (QTile / 8); idx += BThreads) {
-      const int c = idx / (QTile / 8), u = idx % (QTile / 8);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int idx = tid + i * BThreads, c = idx / (QTile / 8), u = idx % (QTile / 8);
       const int64_t off = tbase + static_cast<int64_t>(c) * Lp + q0 + u * 8;
-      *reinterpret_cast<half8*>(&qt[c][u * 8]) = *reinterpret_cast<const half8*>(a.QsT + off);
-      *reinterpret_cast<half8*>(&gt[c][u * 8]) = *reinterpret_cast<const half8*>(a.dOT + off);
+      pqt[i] = *reinterpret_cast<const half8*>(a.QsT + off);
+      pgt[i] = *reinterpret_cast<const half8*>(a.dOT + off);
     }
     if (tid < QTile) {
       const int q = q0 + tid;
-      ls[tid] = q < L ? a.lse[sbase + q] : __builtin_inff();
-      ds[tid] = q < L ? a.D[sbase + q] : 0.f;
+      pl = q < L ? a.lse[sbase + q] : __builtin_inff();
+      pd = q < L ? a.D[sbase + q] : 0.f;
     }
-    __syncthreads();
+  };
+  auto store = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int idx = tid + i * BThreads, r = idx / (DH / 8), c8 = idx % (DH / 8);
+      *reinterpret_cast<half8*>(&qs[st][r][c8 * 8]) = pq[i];
+      *reinterpret_cast<half8*>(&gs[st][r][c8 * 8]) = pg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int idx = tid + i * BThreads, c = idx / (QTile / 8), u = idx % (QTile / 8);
+      *reinterpret_cast<half8*>(&qt[st][c][u * 8]) = pqt[i];
+      *reinterpret_cast<half8*>(&gt[st][c][u * 8]) = pgt[i];
+    }
+    if (tid < QTile) {
+      ls[st][tid] = pl;
+      ds[st][tid] = pd;
+    }
+  };
+  if (qt0 < qt1) {
+    load(qt0 * QTile);
+    store(0);
+  }
+  __syncthreads();
+  for (int qti = qt0; qti < qt1; ++qti) {
+    const int q0 = qti * QTile, stg = (qti - qt0) & 1;
+    const bool more = qti + 1 < qt1;
+    if (more) load(q0 + QTile);
     // Visible pairs in (query tile) x (the wave's 32 keys): causal needs kw0 <= q0 + 31,
     // window also q0 < kw0 + 31 + window.
     bool act = true, edge = q0 + QTile > L || kw0 + 32 > L;
@@ -286,34 +342,37 @@ __global__ __launch_bounds__(BThreads) void bwd_dkdv_kernel(AttnBwdArgs a) {
       act = act && (q0 < kw0 + 31 + window);
       edge |= q0 + QTile - 1 >= kw0 + window;
     }
-    if (!act) continue;
+    if (act) {
     floatx16 s, dp;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
     for (int st = 0; st < NKS; ++st) {
       const int qr = sigma(l32), col = (2 * st + hf) * 8;
-      s = mfma32(*reinterpret_cast<const half8*>(&qs[qr][col]), kf[st], s);
-      dp = mfma32(*reinterpret_cast<const half8*>(&gs[qr][col]), vf[st], dp);
+      s = mfma32(*reinterpret_cast<const half8*>(&qs[stg][qr][col]), kf[st], s);
+      dp = mfma32(*reinterpret_cast<const half8*>(&gs[stg][qr][col]), vf[st], dp);
     }
     // Lane (l32, hf), accumulator r: key krow, query q0 + 16*hf + r.
     half8 pf[2], sf[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int qi = 16 * hf + r;
-      float p = fast_exp2(s[r] - ls[qi]);
+      float p = fast_exp2(s[r] - ls[stg][qi]);
       if (edge && !seen<MASK>(q0 + qi, krow, L, window)) p = 0.f;
       pf[r >> 3][r & 7] = static_cast<half_t>(p);
-      sf[r >> 3][r & 7] = static_cast<half_t>(p * (dp[r] - ds[qi]));
+      sf[r >> 3][r & 7] = static_cast<half_t>(p * (dp[r] - ds[stg][qi]));
     }
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const int c = cb * 32 + l32, col = 16 * hf + 8 * s2;
-        dv[cb] = mfma32(*reinterpret_cast<const half8*>(&gt[c][col]), pf[s2], dv[cb]);
-        dk[cb] = mfma32(*reinterpret_cast<const half8*>(&qt[c][col]), sf[s2], dk[cb]);
+        dv[cb] = mfma32(*reinterpret_cast<const half8*>(&gt[stg][c][col]), pf[s2], dv[cb]);
+        dk[cb] = mfma32(*reinterpret_cast<const half8*>(&qt[stg][c][col]), sf[s2], dk[cb]);
       }
+    }
+    if (more) store(stg ^ 1);
+    __syncthreads();
   }
   // dv[cb], dk[cb] accumulator r: channel cb*32 + 8*(r/4) + 4*hf + r%4 of key krow.
   if (krow < L) {
