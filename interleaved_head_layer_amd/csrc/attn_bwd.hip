@@ -100,8 +100,11 @@ __global__ __launch_bounds__(BThreads) void bwd_dq_kernel(AttnBwdArgs a) {
   constexpr int NR = KTile * (DH / 8) / BThreads, NT = DH * (KTile / 8) / BThreads;
   static_assert(NR * BThreads == KTile * (DH / 8) && NT * BThreads == DH * (KTile / 8), "tile split");
   const int L = a.L, H = a.H, window = a.window, Lp = a.Lp;
+  // Consecutive logical ids share (b, h) and run on one XCD (its L2 keeps their key tiles);
+  // causal rows get longer with the tile index, so causal launches them longest first.
   const int nqt = (L + QRows - 1) / QRows;
-  const int bh = blockIdx.x / nqt, qt = blockIdx.x % nqt;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lid / nqt, qt = MASK == kMaskCausal ? nqt - 1 - lid % nqt : lid % nqt;
   const int b = bh / H, h = bh % H, q0 = qt * QRows;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int64_t rs = static_cast<int64_t>(H) * DH;
@@ -211,12 +214,13 @@ __global__ __launch_bounds__(BThreads) void bwd_dq_kernel(AttnBwdArgs a) {
         if (edge && !seen<MASK>(qrow, k0 + kb * 32 + 16 * hf + r, L, window)) p = 0.f;
         dsf[kb][r >> 3][r & 7] = static_cast<half_t>(p * (dp[kb][r] - dd));
       }
+    // Channel blocks innermost: consecutive products go to independent accumulators.
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
+        for (int cb = 0; cb < NCB; ++cb)
           acc[cb] = mfma32(*reinterpret_cast<const half8*>(&kt[stg][cb * 32 + l32][kb * 32 + 16 * hf + 8 * s2]),
                            dsf[kb][s2], acc[cb]);
     }
@@ -250,8 +254,10 @@ __global__ __launch_bounds__(BThreads) void bwd_dkdv_kernel(AttnBwdArgs a) {
   constexpr int NR = QTile * (DH / 8) / BThreads, NT = DH * (QTile / 8) / BThreads;
   static_assert(NR * BThreads == QTile * (DH / 8) && NT * BThreads == DH * (QTile / 8), "tile split");
   const int L = a.L, H = a.H, window = a.window, Lp = a.Lp;
+  // Key block 0 sees the most queries: ascending ids run the longest first.
   const int nkt = (L + KRows - 1) / KRows;
-  const int bh = blockIdx.x / nkt, kti = blockIdx.x % nkt;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lid / nkt, kti = lid % nkt;
   const int b = bh / H, h = bh % H, k0 = kti * KRows;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int64_t rs = static_cast<int64_t>(H) * DH;
