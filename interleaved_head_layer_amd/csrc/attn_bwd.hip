@@ -36,6 +36,11 @@ constexpr int Pad = 8;      // fp16 padding per LDS row (keeps 16-byte rows, spr
 // layout the next product takes as its contracted (B operand) dimension.
 __device__ __forceinline__ int sigma(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
 
+template <int V>
+struct Slot {
+  static constexpr int value = V;
+};
+
 template <int MASK>
 __device__ __forceinline__ bool seen(int q, int k, int L, int window) {
   if (q >= L || k >= L) return false;
@@ -140,46 +145,53 @@ __global__ __launch_bounds__(BThreads) void bwd_dq_kernel(AttnBwdArgs a) {
   if (MASK != kMaskNone) khi = min(L, q0 + QRows);
   if (MASK == kMaskWindow) klo = max(0, q0 - window + 1);
   const int kt0 = klo / KTile, kt1 = (khi + KTile - 1) / KTile;
-  half8 pk[NR], pv[NR], pt[NT];
-  auto load = [&](int k0) {
+  // Two register sets: tile t+2's loads are issued before tile t's products and stored to LDS
+  // after tile t+1's, so each load has two tiles of products to arrive in.
+  half8 pk[2][NR], pv[2][NR], pt[2][NT];
+  auto load = [&](int k0, auto S) {
+    constexpr int z = decltype(S)::value;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const int idx = tid + i * BThreads, r = idx / (DH / 8), c8 = idx % (DH / 8), key = k0 + r;
-      pk[i] = pv[i] = half8{};
+      pk[z][i] = pv[z][i] = half8{};
       if (key < L) {
         const int64_t off = rbase + static_cast<int64_t>(key) * rs + c8 * 8;
-        pk[i] = *reinterpret_cast<const half8*>(a.K + off);
-        pv[i] = *reinterpret_cast<const half8*>(a.V + off);
+        pk[z][i] = *reinterpret_cast<const half8*>(a.K + off);
+        pv[z][i] = *reinterpret_cast<const half8*>(a.V + off);
       }
     }
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       const int idx = tid + i * BThreads, c = idx / (KTile / 8), u = idx % (KTile / 8);
-      pt[i] = *reinterpret_cast<const half8*>(a.KT + tbase + static_cast<int64_t>(c) * Lp + k0 + u * 8);
+      pt[z][i] = *reinterpret_cast<const half8*>(a.KT + tbase + static_cast<int64_t>(c) * Lp + k0 + u * 8);
     }
   };
-  auto store = [&](int st) {
+  auto store = [&](int st, auto S) {
+    constexpr int z = decltype(S)::value;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const int idx = tid + i * BThreads, r = idx / (DH / 8), c8 = idx % (DH / 8);
-      *reinterpret_cast<half8*>(&ks[st][r][c8 * 8]) = pk[i];
-      *reinterpret_cast<half8*>(&vs[st][r][c8 * 8]) = pv[i];
+      *reinterpret_cast<half8*>(&ks[st][r][c8 * 8]) = pk[z][i];
+      *reinterpret_cast<half8*>(&vs[st][r][c8 * 8]) = pv[z][i];
     }
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       const int idx = tid + i * BThreads, c = idx / (KTile / 8), u = idx % (KTile / 8);
-      *reinterpret_cast<half8*>(&kt[st][c][u * 8]) = pt[i];
+      *reinterpret_cast<half8*>(&kt[st][c][u * 8]) = pt[z][i];
     }
   };
   if (kt0 < kt1) {
-    load(kt0 * KTile);
-    store(0);
+    load(kt0 * KTile, Slot<0>{});
+    store(0, Slot<0>{});
   }
+  if (kt0 + 1 < kt1) load((kt0 + 1) * KTile, Slot<1>{});
   __syncthreads();
-  for (int kti = kt0; kti < kt1; ++kti) {
-    const int k0 = kti * KTile, stg = (kti - kt0) & 1;
-    const bool more = kti + 1 < kt1;
-    if (more) load(k0 + KTile);
+  // Tile kti (parity stg from kt0) is in LDS stage stg; tile kti + 1 is in register set
+  // stg ^ 1; set stg is free for tile kti + 2.
+  auto step = [&](int kti, auto P) {
+    constexpr int stg = decltype(P)::value;
+    const int k0 = kti * KTile;
+    if (kti + 2 < kt1) load(k0 + 2 * KTile, P);
     // Tiles with no visible key for the wave's rows are skipped; only tiles that cross a mask
     // edge or the end of the sequence test each pair.
     bool act = true, edge = k0 + KTile > L || r0 + 32 > L;
@@ -225,8 +237,12 @@ __global__ __launch_bounds__(BThreads) void bwd_dq_kernel(AttnBwdArgs a) {
                            dsf[kb][s2], acc[cb]);
     }
     // The other stage was last read before the previous barrier.
-    if (more) store(stg ^ 1);
+    if (kti + 1 < kt1) store(stg ^ 1, Slot<stg ^ 1>{});
     __syncthreads();
+  };
+  for (int kti = kt0; kti < kt1; kti += 2) {
+    step(kti, Slot<0>{});
+    if (kti + 1 < kt1) step(kti + 1, Slot<1>{});
   }
   // acc[cb] accumulator r: channel cb*32 + 8*(r/4) + 4*hf + r%4 of query qrow.
   if (qrow < L) {
@@ -284,59 +300,62 @@ __global__ __launch_bounds__(BThreads) void bwd_dkdv_kernel(AttnBwdArgs a) {
   if (MASK != kMaskNone) qlo = k0;
   if (MASK == kMaskWindow) qhi = min(L, k0 + KRows - 1 + window);
   const int qt0 = qlo / QTile, qt1 = (qhi + QTile - 1) / QTile;
-  half8 pq[NR], pg[NR], pqt[NT], pgt[NT];
-  float pl = 0.f, pd = 0.f;
-  auto load = [&](int q0) {
+  half8 pq[2][NR], pg[2][NR], pqt[2][NT], pgt[2][NT];  // two register sets, as in the dQ kernel
+  float pl[2] = {0.f, 0.f}, pd[2] = {0.f, 0.f};
+  auto load = [&](int q0, auto S) {
+    constexpr int z = decltype(S)::value;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const int idx = tid + i * BThreads, r = idx / (DH / 8), c8 = idx % (DH / 8), q = q0 + r;
-      pq[i] = pg[i] = half8{};
+      pq[z][i] = pg[z][i] = half8{};
       if (q < L) {
         const int64_t off = rbase + static_cast<int64_t>(q) * rs + c8 * 8;
-        pq[i] = *reinterpret_cast<const half8*>(a.Qs + off);
-        pg[i] = *reinterpret_cast<const half8*>(a.dO + off);
+        pq[z][i] = *reinterpret_cast<const half8*>(a.Qs + off);
+        pg[z][i] = *reinterpret_cast<const half8*>(a.dO + off);
       }
     }
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       const int idx = tid + i * BThreads, c = idx / (QTile / 8), u = idx % (QTile / 8);
       const int64_t off = tbase + static_cast<int64_t>(c) * Lp + q0 + u * 8;
-      pqt[i] = *reinterpret_cast<const half8*>(a.QsT + off);
-      pgt[i] = *reinterpret_cast<const half8*>(a.dOT + off);
+      pqt[z][i] = *reinterpret_cast<const half8*>(a.QsT + off);
+      pgt[z][i] = *reinterpret_cast<const half8*>(a.dOT + off);
     }
     if (tid < QTile) {
       const int q = q0 + tid;
-      pl = q < L ? a.lse[sbase + q] : __builtin_inff();
-      pd = q < L ? a.D[sbase + q] : 0.f;
+      pl[z] = q < L ? a.lse[sbase + q] : __builtin_inff();
+      pd[z] = q < L ? a.D[sbase + q] : 0.f;
     }
   };
-  auto store = [&](int st) {
+  auto store = [&](int st, auto S) {
+    constexpr int z = decltype(S)::value;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const int idx = tid + i * BThreads, r = idx / (DH / 8), c8 = idx % (DH / 8);
-      *reinterpret_cast<half8*>(&qs[st][r][c8 * 8]) = pq[i];
-      *reinterpret_cast<half8*>(&gs[st][r][c8 * 8]) = pg[i];
+      *reinterpret_cast<half8*>(&qs[st][r][c8 * 8]) = pq[z][i];
+      *reinterpret_cast<half8*>(&gs[st][r][c8 * 8]) = pg[z][i];
     }
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       const int idx = tid + i * BThreads, c = idx / (QTile / 8), u = idx % (QTile / 8);
-      *reinterpret_cast<half8*>(&qt[st][c][u * 8]) = pqt[i];
-      *reinterpret_cast<half8*>(&gt[st][c][u * 8]) = pgt[i];
+      *reinterpret_cast<half8*>(&qt[st][c][u * 8]) = pqt[z][i];
+      *reinterpret_cast<half8*>(&gt[st][c][u * 8]) = pgt[z][i];
     }
     if (tid < QTile) {
-      ls[st][tid] = pl;
-      ds[st][tid] = pd;
+      ls[st][tid] = pl[z];
+      ds[st][tid] = pd[z];
     }
   };
   if (qt0 < qt1) {
-    load(qt0 * QTile);
-    store(0);
+    load(qt0 * QTile, Slot<0>{});
+    store(0, Slot<0>{});
   }
+  if (qt0 + 1 < qt1) load((qt0 + 1) * QTile, Slot<1>{});
   __syncthreads();
-  for (int qti = qt0; qti < qt1; ++qti) {
-    const int q0 = qti * QTile, stg = (qti - qt0) & 1;
-    const bool more = qti + 1 < qt1;
-    if (more) load(q0 + QTile);
+  auto step = [&](int qti, auto P) {
+    constexpr int stg = decltype(P)::value;
+    const int q0 = qti * QTile;
+    if (qti + 2 < qt1) load(q0 + 2 * QTile, P);
     // Visible pairs in (query tile) x (the wave's 32 keys): causal needs kw0 <= q0 + 31,
     // window also q0 < kw0 + 31 + window.
     bool act = true, edge = q0 + QTile > L || kw0 + 32 > L;
@@ -377,8 +396,12 @@ __global__ __launch_bounds__(BThreads) void bwd_dkdv_kernel(AttnBwdArgs a) {
         dk[cb] = mfma32(*reinterpret_cast<const half8*>(&qt[stg][c][col]), sf[s2], dk[cb]);
       }
     }
-    if (more) store(stg ^ 1);
+    if (qti + 1 < qt1) store(stg ^ 1, Slot<stg ^ 1>{});
     __syncthreads();
+  };
+  for (int qti = qt0; qti < qt1; qti += 2) {
+    step(qti, Slot<0>{});
+    if (qti + 1 < qt1) step(qti + 1, Slot<1>{});
   }
   // dv[cb], dk[cb] accumulator r: channel cb*32 + 8*(r/4) + 4*hf + r%4 of key krow.
   if (krow < L) {
