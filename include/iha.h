@@ -1,6 +1,7 @@
 /*
  * iha.h - C ABI of the MI355X (gfx950) library for the forward pass of
- * Interleaved Head Attention (IHA).
+ * Interleaved Head Attention (IHA), and for the gradients of its attention step
+ * (iha_attention_backward, below).
  *
  * What is computed: Algorithm 1 of the "Interleaved Head Attention" page
  * (section 4; arXiv 2602.21371), for one layer and a batch of sequences:
