@@ -53,45 +53,53 @@ __device__ __forceinline__ bool seen(int q, int k, int L, int window) {
 // Q*scale rounded to fp16 in row-major form.  One workgroup per (64-row tile, h, b).
 template <int DH>
 __global__ __launch_bounds__(BThreads) void bwd_prep_kernel(AttnBwdArgs a) {
-  __shared__ __attribute__((aligned(16))) half_t tile[64][DH + Pad];
-  constexpr int CH = DH / 8;
+  // All four tensors' rows are loaded at once (one round trip), staged in LDS, then written
+  // channel-major.
+  __shared__ __attribute__((aligned(16))) half_t tile[4][64][DH + Pad];
+  constexpr int CH = DH / 8, NL = 64 * CH / BThreads;  // 16-byte chunks per thread and tensor
+  static_assert(NL * BThreads == 64 * CH, "tile split");
   const int l0 = blockIdx.x * 64, h = blockIdx.y, b = blockIdx.z;
   const int L = a.L, H = a.H;
   const int64_t rs = static_cast<int64_t>(H) * DH;
+  half8 v[4][NL];
+#pragma unroll
   for (int t = 0; t < 4; ++t) {
     const half_t* src = t == 0 ? a.Q : t == 1 ? a.K : t == 2 ? a.V : a.dO;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int idx = threadIdx.x + i * BThreads, r = idx / CH, c8 = idx % CH, l = l0 + r;
+      v[t][i] = half8{};
+      if (l < L) v[t][i] = *reinterpret_cast<const half8*>(src + (static_cast<int64_t>(b) * L + l) * rs + h * DH + c8 * 8);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int idx = threadIdx.x + i * BThreads, r = idx / CH, c8 = idx % CH, l = l0 + r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[0][i][e] = static_cast<half_t>(static_cast<float>(v[0][i][e]) * a.scale);
+    if (l < L) *reinterpret_cast<half8*>(a.Qs + (static_cast<int64_t>(b) * L + l) * rs + h * DH + c8 * 8) = v[0][i];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) *reinterpret_cast<half8*>(&tile[t][r][c8 * 8]) = v[t][i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
     half_t* dst = t == 0 ? a.QsT : t == 1 ? a.KT : t == 2 ? a.VT : a.dOT;
     const int ld = t == 2 ? L : a.Lp;
-    for (int idx = threadIdx.x; idx < 64 * CH; idx += BThreads) {
-      const int r = idx / CH, c8 = idx % CH, l = l0 + r;
-      half8 v = {};
-      if (l < L) {
-        const int64_t off = (static_cast<int64_t>(b) * L + l) * rs + h * DH + c8 * 8;
-        v = *reinterpret_cast<const half8*>(src + off);
-        if (t == 0) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = static_cast<half_t>(static_cast<float>(v[e]) * a.scale);
-          *reinterpret_cast<half8*>(a.Qs + off) = v;
-        }
-      }
-      *reinterpret_cast<half8*>(&tile[r][c8 * 8]) = v;
-    }
-    __syncthreads();
     half_t* base = dst + static_cast<int64_t>(b * H + h) * DH * ld;
     for (int idx = threadIdx.x; idx < DH * 8; idx += BThreads) {
       const int c = idx % DH, u = idx / DH, l = l0 + 8 * u;
       if (l >= ld) continue;
-      half8 v;
+      half8 w;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = tile[8 * u + e][c];
+      for (int e = 0; e < 8; ++e) w[e] = tile[t][8 * u + e][c];
       half_t* p = base + static_cast<int64_t>(c) * ld + l;
       if (t != 2 || ((L & 7) == 0 && l + 8 <= L)) {
-        *reinterpret_cast<half8*>(p) = v;
+        *reinterpret_cast<half8*>(p) = w;
       } else {
-        for (int e = 0; e < 8 && l + e < L; ++e) p[e] = v[e];
+        for (int e = 0; e < 8 && l + e < L; ++e) p[e] = w[e];
       }
     }
-    __syncthreads();
   }
 }
 
