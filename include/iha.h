@@ -57,9 +57,20 @@
  * Errors.  Argument problems are detected on the host before anything is
  * enqueued; X_out is then left untouched.  HIP launch failures give
  * IHA_ERR_DEVICE.  With IHA_FLAG_CHECK the call synchronises `stream` and
- * reports device-detected problems: a non-finite output (a non-finite input,
- * or a value beyond the fp16 range in the IHA_BF16 path) as IHA_ERR_NONFINITE,
- * and an empty allowed set as IHA_ERR_EMPTY_ROW.
+ * reports device-detected problems, in this order of precedence: an empty
+ * allowed set (IHA_ERR_EMPTY_ROW), a non-finite value in X, W_*, alpha_* or R
+ * (IHA_ERR_NONFINITE), an fp16 range overflow (IHA_ERR_RANGE, below), and a
+ * non-finite value in X_out (IHA_ERR_NONFINITE).
+ *
+ * fp16 range (IHA_BF16).  The matrix-core operands are fp16, whose largest finite
+ * magnitude is 65504.  Valid inputs for this path keep these within it: every
+ * per-head projection X W^(m), every mixed value Q~ * log2(e)/sqrt(d), K~ and V~,
+ * and every entry of alpha_* and R (the mixing and the collapse split them into
+ * fp16 high and low parts).  Inputs of the pages' scale (X ~ N(0,1), W ~ N(0,1/D),
+ * alpha ~ N(0,1/H)) stay four orders of magnitude inside it.  With
+ * IHA_FLAG_CHECK an input that leaves it returns IHA_ERR_RANGE; without the flag
+ * the call returns IHA_OK and the affected outputs of X_out are inf or NaN (the
+ * library never rescales silently).  The IHA_F32 path has no such limit.
  */
 #ifndef IHA_H
 #define IHA_H
@@ -81,7 +92,8 @@ typedef enum {
   IHA_ERR_NONFINITE = 4,    /* IHA_FLAG_CHECK: a non-finite value reached the output */
   IHA_ERR_WORKSPACE = 5,    /* workspace missing or smaller than iha_workspace_bytes() */
   IHA_ERR_UNSUPPORTED = 6,  /* head width d (or H) not compiled for this dtype */
-  IHA_ERR_DEVICE = 7        /* a HIP call failed */
+  IHA_ERR_DEVICE = 7,       /* a HIP call failed */
+  IHA_ERR_RANGE = 8         /* IHA_FLAG_CHECK: an fp16 operand exceeded 65504 (see "fp16 range") */
 } iha_status;
 
 typedef enum { IHA_MASK_NONE = 0, IHA_MASK_CAUSAL = 1, IHA_MASK_WINDOW = 2 } iha_mask_mode;

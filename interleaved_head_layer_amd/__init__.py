@@ -6,8 +6,9 @@ package is its thin Python binding plus the seeded synthetic workloads used by t
 tests and the benchmark.
 """
 from ._binding import (IHA_BF16, IHA_F32, IHA_FLAG_CHECK, IHA_MASK_CAUSAL, IHA_MASK_NONE,
-                       IHA_MASK_WINDOW, IHA_PLAN_MIX_FUSED, IHAError, LIB_PATH, TIMED_EVENTS,
-                       iha_attention, iha_attention_backward, iha_forward, iha_plan, iha_status_str, iha_workspace_bytes,
+                       IHA_MASK_WINDOW, IHA_PLAN_MIX_FUSED, IHAError, LIB_PATH,
+                       TIMED_EVENTS, iha_attention, iha_attention_backward, iha_forward,
+                       iha_plan, iha_status_str, iha_workspace_bytes,
                        load_library, make_problem)
 
 __all__ = ["iha_forward", "iha_attention", "iha_attention_backward", "iha_plan", "iha_workspace_bytes", "iha_status_str",

@@ -14,7 +14,8 @@ LIB_PATH = os.path.join(_PKG, "libiha.so")
 
 IHA_OK = 0
 STATUS_NAMES = ["IHA_OK", "IHA_ERR_INVALID_ARG", "IHA_ERR_SHAPE", "IHA_ERR_EMPTY_ROW",
-                "IHA_ERR_NONFINITE", "IHA_ERR_WORKSPACE", "IHA_ERR_UNSUPPORTED", "IHA_ERR_DEVICE"]
+                "IHA_ERR_NONFINITE", "IHA_ERR_WORKSPACE", "IHA_ERR_UNSUPPORTED", "IHA_ERR_DEVICE",
+                "IHA_ERR_RANGE"]
 IHA_MASK_NONE, IHA_MASK_CAUSAL, IHA_MASK_WINDOW = 0, 1, 2
 IHA_F32, IHA_BF16 = 0, 1
 IHA_FLAG_CHECK = 1

@@ -214,9 +214,10 @@ __device__ __forceinline__ void attn_tile(bool edge, const half_t* __restrict__ 
         if (!visible<MASK>(qrow, k0 + kb * 32 + 16 * hf + r, L, window)) s[kb][r] = -__builtin_inff();
   }
   half8 pf[2][2];
+  // Row sums in fp32 from the unrounded probabilities: plain adds overlap the matrix-core
+  // products, whereas a packed fp16 dot product stalls them (measured on gfx950).
   auto probs = [&]() __attribute__((always_inline)) {
-    const half2v ones = {static_cast<half_t>(1.f), static_cast<half_t>(1.f)};
-    float psum = 0.f;
+    float psum0 = 0.f, psum1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -225,9 +226,10 @@ __device__ __forceinline__ void attn_tile(bool edge, const half_t* __restrict__ 
         const half2v pr = __builtin_convertvector(e2, half2v);
         pf[kb][r >> 3][r & 7] = pr[0];
         pf[kb][r >> 3][(r & 7) + 1] = pr[1];
-        psum = __builtin_amdgcn_fdot2(pr, ones, psum, false);
+        psum0 += e2[0];
+        psum1 += e2[1];
       }
-    return psum;
+    return psum0 + psum1;
   };
   // Slow path: a row without an offset yet (its first visible keys), or a tile whose
   // probabilities relative to the offset grew past 2^12 in sum (some p > 2^7 could approach
@@ -405,7 +407,7 @@ __device__ __forceinline__ void first_rows(const AttnArgs& a, int b, int h, floa
     for (int u = 0; u < CU; ++u) acc[u] = fmaf(p, vs[n][g + EGroup * u], acc[u]);
   }
   if (r < R) {
-    float* dst = a.Pe + static_cast<int64_t>(b) * R * D + static_cast<int64_t>(r) * D + h * DH;
+    float* dst = a.Pe + static_cast<int64_t>(b) * a.R2 * D + static_cast<int64_t>(r) * D + h * DH;
 #pragma unroll
     for (int u = 0; u < CU; ++u) dst[g + EGroup * u] = acc[u] * inv;
   }
@@ -531,7 +533,18 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
       if (a.flag) atomicOr(a.flag, kFlagEmptyRow);
     }
     const int64_t orow = obase + static_cast<int64_t>(qrow) * rs;
-    if (a.Oh) {  // fp16 output
+    if (qrow >= a.R && qrow < a.R2) {  // early rows with fp32 outputs: [B][R2][H][d]
+      float* dst = a.Pe + (static_cast<int64_t>(b) * a.R2 + qrow) * rs + h * DH;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          floatx4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = st.o[cb][4 * q + e] * inv;
+          *reinterpret_cast<floatx4*>(dst + cb * 32 + 8 * q + 4 * hf) = v;
+        }
+    } else if (a.Oh) {  // fp16 output
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -614,6 +627,7 @@ template <int DH, int MASK>
 hipError_t launch_f16_impl(const AttnArgs& a, hipStream_t s) {
   const int nqt = (a.L + ABM - 1) / ABM;
   if (a.R < 0 || a.R > kPreciseRows || (a.R > 0 && MASK == kMaskNone)) return hipErrorInvalidValue;
+  if (a.R2 < a.R || a.R2 > a.L || (a.R2 > a.R && !a.Pe)) return hipErrorInvalidValue;
   const int ne = a.R > 0 ? a.H * a.B : 0;  // first-row workgroups
   const dim3 grid(ne + nqt * a.H * a.B);
   // Buffer loads: 16-byte aligned V^T rows (L % 8 == 0) and 32-bit byte offsets within one

@@ -176,52 +176,22 @@ __global__ __launch_bounds__(256) void collapse_h_kernel(CollapseSrc src, const 
 // token's [H*P][d] fp16 block in LDS (row stride d + 4 halves: the operand reads of rows q
 // and q + 8 fall on disjoint banks) and reads B transposed, 8 consecutive q per lane; the
 // next token's block is loaded into registers while the current one is multiplied.
-// A token whose stacked rows include fp32 first rows (the first T0 tokens of a sequence) is
-// collapsed in fp32 on the vector units by a whole workgroup, a thread per (head, 4
-// channels): the first `ne` workgroups stride over those tokens, the others over the rest.
+// A token whose stacked rows include fp32 rows (stacked rows i < R of a sequence: its first
+// T0 = ceil(R / P) tokens) is staged as two fp16 blocks, the high and low parts of each fp32
+// value (low part zero for its fp16 rows), and takes a third product Rt_hi * low; these
+// tokens come first, one at a time per workgroup.
 template <int KS, int NW>
 __global__ __launch_bounds__(NW * 64) void collapse_mfma_kernel(CollapseSrc src, const float* __restrict__ R,
                                                                float* __restrict__ out, int ntok, int H, int P,
-                                                               int d, int ne) {
+                                                               int d) {
   constexpr int NT = NW * 64;
-  extern __shared__ __attribute__((aligned(16))) uint16_t pl[];  // [KS*16][d + 4]
+  extern __shared__ __attribute__((aligned(16))) uint16_t pl[];  // 2 x [KS*16][d + 4]: value, low part
   const int HP = H * P, ld = d + 4, N = src.N, T0 = src.T0;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
-
-  if (static_cast<int>(blockIdx.x) < ne) {
-    // First-row tokens: rows i < R from the fp32 rows Pe [B][R][H][d], the rest fp16.
-    const int nearly = (ntok / N) * T0;
-    for (int e = blockIdx.x; e < nearly; e += ne) {
-      const int tok = (e / T0) * N + e % T0, t = e % T0;
-      const int64_t eb = static_cast<int64_t>(tok / N) * src.R;
-      const int quads = d / 4;
-      for (int u = tid; u < H * quads; u += NT) {
-        const int h = u / quads, c4 = (u % quads) * 4;
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-        for (int q = 0; q < HP; ++q) {
-          const int j = q / H, hp = q % H, i = t * P + j;
-          floatx4 pv;
-          if (i < src.R) {
-            pv = *reinterpret_cast<const floatx4*>(src.Pe + ((eb + i) * H + hp) * d + c4);
-          } else {
-            const half4 v = *reinterpret_cast<const half4*>(src.Ph + (static_cast<int64_t>(tok) * HP + q) * d + c4);
-            pv = floatx4{static_cast<float>(v[0]), static_cast<float>(v[1]), static_cast<float>(v[2]),
-                         static_cast<float>(v[3])};
-          }
-          const float r = R[h * HP + hp * P + j];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) acc[c] = fmaf(r, pv[c], acc[c]);
-        }
-        *reinterpret_cast<floatx4*>(out + static_cast<int64_t>(tok) * H * d + h * d + c4) = acc;
-      }
-    }
-    return;
-  }
-  const int g0 = blockIdx.x - ne, ng = gridDim.x - ne;  // this workgroup among the fp16 ones
+  uint16_t* pl2 = pl + KS * 16 * ld;
 
   // Rows HP .. KS*16-1 stay zero (their A columns are zero too, but LDS must hold no NaN).
-  for (int i = HP * ld + tid; i < KS * 16 * ld; i += NT) pl[i] = 0;
+  for (int i = HP * ld + tid; i < KS * 16 * ld; i += NT) pl[i] = pl2[i] = 0;
   half8 ah[KS], al[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
@@ -235,13 +205,75 @@ __global__ __launch_bounds__(NW * 64) void collapse_mfma_kernel(CollapseSrc src,
   const int c0 = w * 32;
   const int cpr = d / 8;     // 16-byte chunks per stacked row
   const int nch = HP * cpr;  // chunks per token (<= KS * NT)
-  // The workgroup's fp16 tokens: tok = g0 + k * ng with t >= T0.
+  auto store_out = [&](int tok, const floatx16& acc) {
+    float* dst = out + static_cast<int64_t>(tok) * H * d + c0 + l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int h = 8 * (r >> 2) + 4 * hf + (r & 3);
+      if (h < H) dst[static_cast<int64_t>(h) * d] = acc[r];
+    }
+  };
+
+  // Tokens with fp32 rows: high/low fp16 blocks, three products per k-step.
+  const int nearly = (ntok / N) * T0;
+  for (int e = blockIdx.x; e < nearly; e += gridDim.x) {
+    const int tok = (e / T0) * N + e % T0, t = e % T0;
+    const int64_t eb = static_cast<int64_t>(tok / N) * src.R;
+    for (int ch = tid; ch < nch; ch += NT) {
+      const int q = ch / cpr, c8 = (ch % cpr) * 8;
+      const int i = t * P + q / H;
+      half8 hi, lo;
+      if (i < src.R) {
+        const float* p = src.Pe + ((eb + i) * H + q % H) * d + c8;
+        const floatx4 a = *reinterpret_cast<const floatx4*>(p), b = *reinterpret_cast<const floatx4*>(p + 4);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float v = k < 4 ? a[k] : b[k - 4];
+          hi[k] = static_cast<half_t>(v);
+          lo[k] = static_cast<half_t>(v - static_cast<float>(hi[k]));
+        }
+      } else {
+        hi = *reinterpret_cast<const half8*>(src.Ph + (static_cast<int64_t>(tok) * HP + q) * d + c8);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) lo[k] = static_cast<half_t>(0.f);
+      }
+      uint2* dh = reinterpret_cast<uint2*>(pl + q * ld + c8);  // 8-byte aligned
+      uint2* dl = reinterpret_cast<uint2*>(pl2 + q * ld + c8);
+      const uint4 hb = __builtin_bit_cast(uint4, hi), lb = __builtin_bit_cast(uint4, lo);
+      dh[0] = make_uint2(hb.x, hb.y);
+      dh[1] = make_uint2(hb.z, hb.w);
+      dl[0] = make_uint2(lb.x, lb.y);
+      dl[1] = make_uint2(lb.z, lb.w);
+    }
+    __syncthreads();
+    floatx16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      half8 b, b2;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int row = (ks * 16 + 8 * hf + k) * ld + c0 + l32;
+        b[k] = __builtin_bit_cast(half_t, pl[row]);
+        b2[k] = __builtin_bit_cast(half_t, pl2[row]);
+      }
+      acc = mfma32(ah[ks], b, acc);
+      acc = mfma32(al[ks], b, acc);
+      acc = mfma32(ah[ks], b2, acc);
+    }
+    __syncthreads();  // the next token's staging overwrites both blocks
+    store_out(tok, acc);
+  }
+
+  // The other tokens: tok = blockIdx.x + k * gridDim.x with t >= T0, fp16 blocks only.
+  const int ng = gridDim.x;
   auto next_tok = [&](int tok) {
     for (tok += ng; tok < ntok && tok % N < T0; tok += ng) {
     }
     return tok;
   };
-  int tok = g0;
+  int tok = blockIdx.x;
   if (tok < ntok && tok % N < T0) tok = next_tok(tok);
   uint4 buf[KS];
   auto load = [&](int tk) {
@@ -276,12 +308,7 @@ __global__ __launch_bounds__(NW * 64) void collapse_mfma_kernel(CollapseSrc src,
       acc = mfma32(al[ks], b, acc);
     }
     __syncthreads();  // the next token's staging overwrites the block
-    float* dst = out + static_cast<int64_t>(tok) * H * d + c0 + l32;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int h = 8 * (r >> 2) + 4 * hf + (r & 3);
-      if (h < H) dst[static_cast<int64_t>(h) * d] = acc[r];
-    }
+    store_out(tok, acc);
     tok = nt;
   }
 }
@@ -322,18 +349,18 @@ hipError_t launch_collapse(const float* Pbar, const float* R, float* out, int nt
 hipError_t launch_collapse_h(const half_t* Ph, const float* Pe, int Rrows, const float* R, float* out, int B,
                              int N, int H, int P, int d, hipStream_t s) {
   const int HP = H * P, KS = (HP + 15) / 16;
-  if (H > 32 || KS > 8 || (d != 64 && d != 128)) {
+  // The matrix-core kernel stages two [KS*16][d + 4] fp16 blocks: at most 64 KB of LDS.
+  if (H > 32 || KS > 8 || (d != 64 && d != 128) || 2 * KS * 16 * (d + 4) * 2 > 65536) {
     const CollapseSrc src{nullptr, Ph, Pe, Rrows, N, 0};
     return launch_h<true>(src, R, out, B * N, H, P, d, s);
   }
   const CollapseSrc src{nullptr, Ph, Pe, Rrows, N, (Rrows + P - 1) / P};
   const int ntok = B * N;
-  // A few workgroups for the first-row tokens, then about 8 fp16 tokens per workgroup.
-  const int ne = std::min(B * src.T0, 256);
-  const int grid = ne + std::max(1, std::min(ntok / 8, 256 * 8 - ne));
-  const size_t lds = static_cast<size_t>(KS) * 16 * (d + 4) * sizeof(uint16_t);
+  // About 8 tokens per workgroup.
+  const int grid = std::max(1, std::min(ntok / 8, 256 * 8));
+  const size_t lds = 2 * static_cast<size_t>(KS) * 16 * (d + 4) * sizeof(uint16_t);
   auto go = [&](auto kern, int threads) {
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, s, src, R, out, ntok, H, P, d, ne);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, s, src, R, out, ntok, H, P, d);
   };
   switch (KS * 4 + d / 64) {  // d / 64 in {1, 2}
 #define IHA_COLLAPSE_CASE(ks)                                                    \

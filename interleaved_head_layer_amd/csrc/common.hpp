@@ -22,8 +22,12 @@ constexpr int kMaskCausal = 1;
 constexpr int kMaskWindow = 2;
 
 // Bits of the device flag word in the workspace.
-constexpr unsigned kFlagEmptyRow = 1u;
-constexpr unsigned kFlagNonFinite = 2u;
+constexpr unsigned kFlagEmptyRow = 1u;       // a valid query saw no key
+constexpr unsigned kFlagNonFinite = 2u;      // a non-finite value reached the output
+constexpr unsigned kFlagRange = 4u;          // an fp16 matrix-core operand left the fp16 range
+constexpr unsigned kFlagInputNonFinite = 8u; // a non-finite input value
+// Largest finite fp16 magnitude.
+constexpr float kF16Max = 65504.f;
 
 __device__ __forceinline__ float bf16_to_float(bf16_bits b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);

@@ -81,12 +81,24 @@ __global__ __launch_bounds__(kFoldThreads) void fold_kernel(FoldArgs a) {
 
 __global__ void clear_flag_kernel(unsigned* flag) { *flag = 0u; }
 
-__global__ __launch_bounds__(256) void check_finite_kernel(const float* __restrict__ x, int64_t n,
-                                                           unsigned* flag) {
-  bool bad = false;
-  for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256)
-    bad |= !__builtin_isfinite(x[i]);
-  if (bad) atomicOr(flag, kFlagNonFinite);
+// Sets `nonfinite_bit` for a non-finite element and kFlagRange for a finite one beyond
+// `limit` in magnitude (limit = +inf: no range test).
+__device__ __forceinline__ float value_of(float v) { return v; }
+__device__ __forceinline__ float value_of(bf16_bits v) { return bf16_to_float(v); }
+__device__ __forceinline__ float value_of(half_t v) { return static_cast<float>(v); }
+
+template <typename T>
+__global__ __launch_bounds__(256) void check_values_kernel(const T* __restrict__ x, int64_t n, unsigned* flag,
+                                                           unsigned nonfinite_bit, float limit) {
+  unsigned bits = 0u;
+  for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256) {
+    const float v = value_of(x[i]);
+    if (!__builtin_isfinite(v))
+      bits |= nonfinite_bit;
+    else if (__builtin_fabsf(v) > limit)
+      bits |= kFlagRange;
+  }
+  if (bits) atomicOr(flag, bits);
 }
 
 template <typename Tin, typename Tout>
@@ -108,10 +120,26 @@ hipError_t launch_clear_flag(unsigned* flag, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_check_finite(const float* x, int64_t n, unsigned* flag, hipStream_t s) {
-  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 256 * 8));
-  hipLaunchKernelGGL(check_finite_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, x,
-                     n, flag);
+hipError_t launch_check_values(const void* x, int kind, int64_t n, unsigned* flag, unsigned nonfinite_bit,
+                               float limit, hipStream_t s) {
+  if (n < 1) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 256 * 8))));
+  switch (kind) {
+    case kValF32:
+      hipLaunchKernelGGL(check_values_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(x), n,
+                         flag, nonfinite_bit, limit);
+      break;
+    case kValBF16:
+      hipLaunchKernelGGL(check_values_kernel<bf16_bits>, grid, dim3(256), 0, s,
+                         static_cast<const bf16_bits*>(x), n, flag, nonfinite_bit, limit);
+      break;
+    case kValF16:
+      hipLaunchKernelGGL(check_values_kernel<half_t>, grid, dim3(256), 0, s, static_cast<const half_t*>(x), n,
+                         flag, nonfinite_bit, limit);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

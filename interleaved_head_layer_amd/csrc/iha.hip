@@ -23,7 +23,8 @@ bool aligned(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p)
 
 struct Layout {
   size_t flag, wt, yqk, yvt, q, k, vt, pbar, pe, qe, ke, vte, ye, total;
-  int R;  // precise first stacked rows (0 when unused)
+  int R;   // precise first stacked rows (0 when unused)
+  int R2;  // stacked rows with fp32 attention outputs (R <= R2; 0 when unused)
 };
 
 bool d_supported(int32_t dtype, int64_t d) {
@@ -87,7 +88,8 @@ Layout layout_of(const iha_problem& p) {
   if (p.dtype == IHA_BF16 && p.mask != IHA_MASK_NONE) {
     const int64_t R = std::min<int64_t>(iha::kPreciseRows, p.P * p.N);
     L.R = static_cast<int>(R);
-    L.pe = take(static_cast<size_t>(p.B) * R * p.D * 4);
+    L.R2 = static_cast<int>(std::min<int64_t>(iha::kF32OutRows, p.P * p.N));
+    L.pe = take(static_cast<size_t>(p.B) * L.R2 * p.D * 4);
     if (iha::fused_shape(p.H, p.D, p.P)) {
       L.ye = take(static_cast<size_t>(p.B) * ((R + p.P - 1) / p.P) * 3 * p.D * 4);
     } else {
@@ -117,11 +119,15 @@ bool log_enabled() {
     }                                                                              \
   } while (0)
 
+// Precedence: an empty row, then a non-finite input, then an fp16 range overflow, then a
+// non-finite output (which without the two causes before it has no other source).
 iha_status read_flag(const unsigned* flag, hipStream_t stream) {
   unsigned host = 0;
   IHA_HIP(hipStreamSynchronize(stream));
   IHA_HIP(hipMemcpy(&host, flag, sizeof(host), hipMemcpyDeviceToHost));
   if (host & iha::kFlagEmptyRow) return IHA_ERR_EMPTY_ROW;
+  if (host & iha::kFlagInputNonFinite) return IHA_ERR_NONFINITE;
+  if (host & iha::kFlagRange) return IHA_ERR_RANGE;
   if (host & iha::kFlagNonFinite) return IHA_ERR_NONFINITE;
   return IHA_OK;
 }
@@ -265,6 +271,7 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
       }
       at.Pe = reinterpret_cast<float*>(ws + lay.pe);
       at.R = lay.R;
+      at.R2 = lay.R2;
       at.P = P;
       at.T0 = (lay.R + P - 1) / P;
       at.escale = score_scale;
@@ -279,14 +286,35 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
 
   // Steps 4-5: unstack, collapse with R, concatenate heads.
   if (bf16)
-    IHA_HIP(iha::launch_collapse_h(at.Oh, lay.R > 0 ? reinterpret_cast<const float*>(ws + lay.pe) : nullptr, lay.R, R,
-                                   X_out, B, N, H, P, d, stream));
+    IHA_HIP(iha::launch_collapse_h(at.Oh, lay.R2 > 0 ? reinterpret_cast<const float*>(ws + lay.pe) : nullptr,
+                                   lay.R2, R, X_out, B, N, H, P, d, stream));
   else
     IHA_HIP(iha::launch_collapse(at.O, R, X_out, B * N, H, P, d, stream));
   if (ev) IHA_HIP(hipEventRecord(ev[6], stream));
 
   if (p.flags & IHA_FLAG_CHECK) {
-    IHA_HIP(iha::launch_check_finite(X_out, static_cast<int64_t>(B) * N * D, flag, stream));
+    // Inputs: non-finite values; for bf16 inputs also alpha and R beyond the fp16 range (the
+    // matrix-core mixing and collapse split them into fp16 high and low parts).  Then the fp16
+    // stacked Q~, K~, V~: with finite inputs a non-finite value there means a projection or
+    // a mixed value beyond the fp16 range.  Last the output.
+    using iha::kFlagInputNonFinite;
+    const int xk = bf16 ? iha::kValBF16 : iha::kValF32;
+    const float lim = bf16 ? iha::kF16Max : __builtin_inff();
+    const int64_t nx = static_cast<int64_t>(B) * N * D, nw = static_cast<int64_t>(D) * D;
+    const int64_t na = static_cast<int64_t>(H) * H * P;
+    IHA_HIP(iha::launch_check_values(X, xk, nx, flag, kFlagInputNonFinite, __builtin_inff(), stream));
+    for (const void* W : {W_Q, W_K, W_V})
+      IHA_HIP(iha::launch_check_values(W, xk, nw, flag, kFlagInputNonFinite, __builtin_inff(), stream));
+    for (const float* a : {alpha_Q, alpha_K, alpha_V})
+      IHA_HIP(iha::launch_check_values(a, iha::kValF32, na, flag, kFlagInputNonFinite, lim, stream));
+    IHA_HIP(iha::launch_check_values(R, iha::kValF32, na, flag, kFlagInputNonFinite, lim, stream));
+    if (bf16) {
+      const int64_t act = static_cast<int64_t>(B) * N * P * D;
+      for (size_t off : {lay.q, lay.k, lay.vt})
+        IHA_HIP(iha::launch_check_values(ws + off, iha::kValF16, act, flag, iha::kFlagRange, __builtin_inff(),
+                                         stream));
+    }
+    IHA_HIP(iha::launch_check_values(X_out, iha::kValF32, nx, flag, iha::kFlagNonFinite, __builtin_inff(), stream));
     return read_flag(flag, stream);
   }
   return IHA_OK;
@@ -466,6 +494,7 @@ const char* iha_status_str(iha_status s) {
     case IHA_ERR_WORKSPACE: return "IHA_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case IHA_ERR_UNSUPPORTED: return "IHA_ERR_UNSUPPORTED: head width or head count not supported";
     case IHA_ERR_DEVICE: return "IHA_ERR_DEVICE: a HIP call failed";
+    case IHA_ERR_RANGE: return "IHA_ERR_RANGE: an intermediate value exceeds the fp16 range";
   }
   return "IHA_ERR_UNKNOWN";
 }

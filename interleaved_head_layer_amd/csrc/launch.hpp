@@ -39,6 +39,9 @@ constexpr int kQKChunked = 1;   // [B][H][d/8][L][8]: 16-byte d-chunks, contiguo
 // bf16 inputs under a causal or window mask: the first kPreciseRows stacked rows of every
 // (b, h) see the fewest keys and have the largest outputs; they are computed again in fp32.
 constexpr int kPreciseRows = 32;
+// ... and their outputs, up to stacked row kF32OutRows of every (b, h), stay fp32 (the fp16
+// rounding of an output is a quarter of its error; outputs of rows with few keys are large).
+constexpr int kF32OutRows = 1024;
 
 // Masked attention over the stacked sequence: O = softmax_2(s) V with base-2 scores
 // s = (q . k) * qk_scale.
@@ -63,8 +66,10 @@ struct AttnArgs {
   const float* Ve;
   const float* Ye;
   const float* alpha[3];
-  float* Pe;
+  float* Pe;       // [B][R2][H][d] fp32: rows < R from the fp32 recomputation, rows R..R2-1
+                   // from the tiled kernel (fp32 instead of fp16)
   int R, P, T0;
+  int R2;          // R <= R2 <= L
   float escale;
   // fp16 kernel: when set, [B][H][L] base-2 log-sum-exp of every row's visible scores
   // (the row's probabilities are exp2(score - lse)); +inf for a row with no visible key.
@@ -154,8 +159,13 @@ hipError_t launch_collapse_h(const half_t* Ph, const float* Pe, int R, const flo
 hipError_t launch_collapse(const float* Pbar, const float* R, float* out, int ntok, int H, int P,
                            int d, hipStream_t s);
 
-// Sets kFlagNonFinite in *flag if any of x[0..n) is not finite.
-hipError_t launch_check_finite(const float* x, int64_t n, unsigned* flag, hipStream_t s);
+// Scans x[0..n) (kind: kValF32, kValBF16 or kValF16 elements): sets `nonfinite_bit` in *flag
+// if an element is not finite, and kFlagRange if a finite one exceeds `limit` in magnitude.
+constexpr int kValF32 = 0;
+constexpr int kValBF16 = 1;
+constexpr int kValF16 = 2;
+hipError_t launch_check_values(const void* x, int kind, int64_t n, unsigned* flag, unsigned nonfinite_bit,
+                               float limit, hipStream_t s);
 // *flag = 0 (a one-thread fill kernel).
 hipError_t launch_clear_flag(unsigned* flag, hipStream_t s);
 

@@ -108,7 +108,9 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
 def make_inputs(w: Workload) -> Dict[str, np.ndarray]:
     """Draw the inputs of workload ``w``.  All arrays are float32 and C-contiguous.
 
-    For bf16 workloads X and W_* hold bf16-representable values.
+    For bf16 workloads X and W_* hold bf16-representable values.  Workloads with
+    repeated rows also return ``repeated_pos``: the sorted flat token indices b*N + t
+    that received the copied row (int64).
     """
     rng = np.random.Generator(np.random.PCG64(w.seed))
     B, N, D, H, P = w.B, w.N, w.D, w.H, w.P
@@ -129,6 +131,7 @@ def make_inputs(w: Workload) -> Dict[str, np.ndarray]:
         aV = aQ.copy()
         R = np.zeros((H, H * P), np.float32)
         R[np.arange(H), np.arange(H) * P] = 1.0
+    pos = None
     if w.repeated_keys:
         row = rng.standard_normal(D, dtype=np.float32)
         pos = rng.choice(B * N, size=w.repeated_keys, replace=False)
@@ -136,7 +139,10 @@ def make_inputs(w: Workload) -> Dict[str, np.ndarray]:
     if w.dtype == "bf16":
         X, WQ, WK, WV = (round_to_bf16(a) for a in (X, WQ, WK, WV))
     out = dict(X=X, WQ=WQ, WK=WK, WV=WV, aQ=aQ, aK=aK, aV=aV, R=R)
-    return {k: np.ascontiguousarray(v, dtype=np.float32) for k, v in out.items()}
+    out = {k: np.ascontiguousarray(v, dtype=np.float32) for k, v in out.items()}
+    if pos is not None:
+        out["repeated_pos"] = np.sort(pos.astype(np.int64))   # flat token indices b*N + t
+    return out
 
 
 def make_params(w: Workload) -> Dict[str, np.ndarray]:

@@ -33,3 +33,14 @@ def read_golden(name):
 @pytest.fixture
 def golden():
     return read_golden
+
+
+@pytest.fixture
+def progress(request):
+    """Print a progress line past pytest's output capture (long oracle runs stay visible)."""
+    capman = request.config.pluginmanager.getplugin("capturemanager")
+
+    def say(msg):
+        with capman.global_and_fixture_disabled():
+            print(f"[progress] {msg}", file=sys.stderr, flush=True)
+    return say

@@ -59,6 +59,12 @@ CASES = [
     (1, 1024, 2, 128, "window", 256),  # several key and query tiles per workgroup
     (1, 600, 2, 128, "window", 100000),  # window beyond the sequence = causal
     (2, 256, 2, 64, "none", 0),
+    # the d = 128 causal kernels over several tiles: two-deep prefetch, longest-first causal
+    # tile order, skipped tiles, ragged tails
+    (2, 333, 2, 128, "causal", 0),
+    (1, 1000, 2, 128, "causal", 0),
+    (1, 1000, 2, 64, "causal", 0),
+    (1, 700, 2, 128, "none", 0),       # no mask, 11 key tiles through the prefetch path
 ]
 
 

@@ -40,6 +40,9 @@ def test_identity_and_repeated_rows():
     rows = x["X"].reshape(-1, 64)
     _, counts = np.unique(rows, axis=0, return_counts=True)
     assert counts.max() == 16
+    pos = x["repeated_pos"]
+    assert pos.dtype == np.int64 and len(np.unique(pos)) == 16
+    assert np.all(rows[pos] == rows[pos[0]])
 
 
 def test_sample_tokens_cover_edges():
