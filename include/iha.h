@@ -161,6 +161,24 @@ iha_status iha_forward_timed(const iha_problem* prob, const void* X, const void*
                              float* X_out, void* workspace, size_t workspace_bytes,
                              hipStream_t stream, hipEvent_t* events);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): iha_forward with its workspace in a
+ * buffer of IHA_STATIC_WORKSPACE_BYTES that the library holds on each device it runs on
+ * (a static device array, created with the library's code object on that device and kept
+ * until the process ends).  The caller passes inputs and X_out as for iha_forward; this
+ * entry point allocates nothing (no hipMalloc, hipFree or allocating library call; the
+ * first call on a device looks the buffer's address up once).  A problem whose
+ * iha_workspace_bytes() exceeds IHA_STATIC_WORKSPACE_BYTES returns IHA_ERR_WORKSPACE
+ * before any launch.  Every call on a device shares that device's buffer and it keeps the
+ * last call's contents (the kernels clear what must start at zero): calls that overlap on
+ * one device - from several threads, or on several streams - race and must be serialised
+ * by the caller. */
+#define IHA_STATIC_WORKSPACE_BYTES (64u << 20)
+iha_status iha_forward_static(const iha_problem* prob, const void* X, const void* W_Q,
+                              const void* W_K, const void* W_V, const float* alpha_Q,
+                              const float* alpha_K, const float* alpha_V, const float* R,
+                              float* X_out, hipStream_t stream);
+
 /* The attention step alone (step 3 of Algorithm 1; textbook eq. 5.3 and 5.11),
  * for already stacked, interleaved tensors of stacked length L:
  *   Q, K   fp16 [B][L][H][d]   (row i = stacked position i)

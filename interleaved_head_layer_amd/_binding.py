@@ -21,6 +21,7 @@ IHA_F32, IHA_BF16 = 0, 1
 IHA_FLAG_CHECK = 1
 IHA_PLAN_MIX_FUSED = 1
 TIMED_EVENTS = 7       # IHA_TIMED_EVENTS in include/iha.h
+STATIC_WORKSPACE_BYTES = 64 << 20   # IHA_STATIC_WORKSPACE_BYTES in include/iha.h
 _MASKS = {"none": IHA_MASK_NONE, "causal": IHA_MASK_CAUSAL, "window": IHA_MASK_WINDOW}
 
 
@@ -89,6 +90,8 @@ def load_library() -> ctypes.CDLL:
         lib.iha_forward.restype = ctypes.c_int
         lib.iha_forward_timed.argtypes = fwd + [ctypes.POINTER(vp)]
         lib.iha_forward_timed.restype = ctypes.c_int
+        lib.iha_forward_static.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.iha_forward_static.restype = ctypes.c_int
         lib.iha_attention.argtypes = [i64, i64, i64, i64, i32, i64, ctypes.c_float, vp, vp, vp, vp,
                                       u32, vp, vp]
         lib.iha_attention.restype = ctypes.c_int
@@ -198,6 +201,34 @@ def iha_forward(X, W_Q, W_K, W_V, alpha_Q, alpha_K, alpha_V, R, H: int, P: int, 
         st = lib.iha_forward_timed(ctypes.byref(prob), *args, stream, evs)
     if st != IHA_OK:
         raise IHAError(st, "iha_forward")
+    return out
+
+
+def iha_forward_static(X, W_Q, W_K, W_V, alpha_Q, alpha_K, alpha_V, R, H: int, P: int, mask_mode,
+                       out, window: Optional[int] = None, flags: int = 0):
+    """iha_forward with the library's static per-device workspace (iha_forward_static): no
+    device memory is allocated, here or in the library; the caller supplies `out`
+    ([B, N, D] fp32).  Problems needing more than STATIC_WORKSPACE_BYTES raise
+    IHAError(IHA_ERR_WORKSPACE); calls that overlap on one device race."""
+    import torch
+    if X.dim() != 3:
+        raise ValueError("X must be [B, N, D]")
+    B, N, D = (int(s) for s in X.shape)
+    dtype = {torch.bfloat16: IHA_BF16, torch.float32: IHA_F32}.get(X.dtype)
+    if dtype is None:
+        raise TypeError("X must be bfloat16 or float32")
+    prob = make_problem(B, N, D, int(H), int(P), mask_mode, window, dtype, flags)
+    args = [_dev_ptr(X, "X")]
+    for n, w in (("W_Q", W_Q), ("W_K", W_K), ("W_V", W_V)):
+        args.append(_dev_ptr(w, n, X.dtype, (D, D)))
+    for n, a in (("alpha_Q", alpha_Q), ("alpha_K", alpha_K), ("alpha_V", alpha_V)):
+        args.append(_dev_ptr(a, n, torch.float32, (H, H, P)))
+    args.append(_dev_ptr(R, "R", torch.float32, (H, H * P)))
+    args.append(_dev_ptr(out, "out", torch.float32, (B, N, D)))
+    stream = ctypes.c_void_p(torch.cuda.current_stream(X.device).cuda_stream)
+    st = load_library().iha_forward_static(ctypes.byref(prob), *args, stream)
+    if st != IHA_OK:
+        raise IHAError(st, "iha_forward_static")
     return out
 
 

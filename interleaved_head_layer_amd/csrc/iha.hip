@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -358,6 +359,32 @@ iha_status bwd_validate(int64_t B, int64_t L, int64_t H, int64_t d, int32_t mask
   return IHA_OK;
 }
 
+// Workspace of iha_forward_static: one copy per device, held until the process ends.  In
+// host code `scratch` names a host-side stand-in, never the device memory: host code uses
+// only the per-device address that hipGetSymbolAddress returns for it.
+constexpr size_t kStaticBytes = IHA_STATIC_WORKSPACE_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device.
+iha_status static_workspace(void** ptr) {
+  int dev = -1;
+  IHA_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return IHA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    IHA_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return IHA_ERR_DEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return IHA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -396,6 +423,20 @@ iha_status iha_forward_timed(const iha_problem* prob, const void* X, const void*
     if (!events[i]) return IHA_ERR_INVALID_ARG;
   return forward_impl(prob, X, W_Q, W_K, W_V, alpha_Q, alpha_K, alpha_V, R, X_out, workspace,
                       workspace_bytes, stream, events);
+}
+
+iha_status iha_forward_static(const iha_problem* prob, const void* X, const void* W_Q,
+                              const void* W_K, const void* W_V, const float* alpha_Q,
+                              const float* alpha_K, const float* alpha_V, const float* R,
+                              float* X_out, hipStream_t stream) {
+  const iha_status v = validate(prob);
+  if (v != IHA_OK) return v;
+  if (layout_of(*prob).total > kStaticBytes) return IHA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const iha_status st = static_workspace(&ws);
+  if (st != IHA_OK) return st;
+  return forward_impl(prob, X, W_Q, W_K, W_V, alpha_Q, alpha_K, alpha_V, R, X_out, ws, kStaticBytes,
+                      stream, nullptr);
 }
 
 iha_status iha_attention(int64_t B, int64_t L, int64_t H, int64_t d, int32_t mask, int64_t window,
