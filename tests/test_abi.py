@@ -29,6 +29,18 @@ def test_library_loads_and_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
+def test_probe_library_exports_its_declared_symbol():
+    """The benchmark's measurement probe (include/iha_probe.h, libiha_probe.so)."""
+    from interleaved_head_layer_amd import build as hb
+    src = open(os.path.join(ROOT, "include", "iha_probe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = sorted(set(re.findall(r"\b(ihp_[a-z_]+)\s*\(", src)))
+    assert names == ["ihp_mfma_rate"]
+    lib = ctypes.CDLL(hb.PROBE_LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
 def test_status_strings():
     for code, name in enumerate(bd.STATUS_NAMES):
         assert bd.iha_status_str(code).startswith(name)
