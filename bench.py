@@ -322,6 +322,39 @@ def run_attention_backward(w, steps, warmup):
             "note": "whole call: prep copies, forward recompute (O, lse), dQ and dK/dV kernels"}
 
 
+def run_nexus_inner(B, L, H, d, mask, steps, warmup):
+    """Time iha_nexus_inner (softmax(Q Q^T / sqrt(d)) Q per head) on fp16 Q [B, L, H, d];
+    work: 4 * d flops per visible (query, key) pair, as for the attention step."""
+    import torch
+    import interleaved_head_layer_amd as iha
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(77)
+    q = torch.randn((B, L, H, d), generator=g, device="cuda:0").half()
+    out = torch.empty((B, L, H, d), dtype=torch.float32, device="cuda:0")
+    lib = iha.load_library()
+    nbytes = ctypes.c_size_t(0)
+    assert lib.iha_nexus_inner_workspace(B, L, H, d, ctypes.byref(nbytes)) == 0
+    ws = torch.empty(int(nbytes.value), dtype=torch.uint8, device="cuda:0")
+    call = lambda: iha.iha_nexus_inner(q, mask, out=out, workspace=ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    code = {"none": 0, "causal": 1}[mask]
+    work = 4.0 * d * B * H * allowed_pairs(L, code, 0)
+    del q, out, ws
+    torch.cuda.empty_cache()
+    return {"shape": {"B": B, "L": L, "H": H, "d": d, "mask": mask}, "ms": round(ms, 4), "steps": steps,
+            "roofline": roof("mfma", work, ms),
+            "note": "whole call: the channel-major copy of Q and the attention kernel"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -420,6 +453,8 @@ def main():
             f2.free()
             extra[name] = entry
         bwd = run_attention_backward(wl.WORKLOADS[OTHERS[0]], args.extra_steps, 3)
+        extra["nexus_inner_causal_b4_l8192_h16"] = run_nexus_inner(4, 8192, 16, 128, "causal",
+                                                                   args.extra_steps, 3)
 
     chip = probe_chip()
     if chip is not None:

@@ -221,6 +221,26 @@ iha_status iha_attention_backward(int64_t B, int64_t L, int64_t H, int64_t d, in
                                   float* dK, float* dV, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
 
+/* The inner attention of the Nexus higher-order attention ("Higher-order attention
+ * mechanisms" page, section 2, the refined query and key: Attention_q(X) =
+ * softmax(Q Q^T / sqrt(d_k)) Q, and the same for K), per head: self-attention whose keys
+ * and values are the queries themselves, on the same tiled kernel as iha_attention.
+ *   Q   fp16 [B][L][H][d]  (row i = position i), 16-byte aligned
+ *   O   float [B][L][H][d] O[i] = sum_{i' visible} softmax_i'(s) Q[i'], 16-byte aligned
+ * with base-2 scores s = (q_i . q_i') * score_scale (pass log2(e)/sqrt(d) for the page's
+ * softmax(Q Q^T / sqrt(d_k))).  mask/window select the visible positions as for
+ * iha_forward (the page's formula has no mask: IHA_MASK_NONE; a causal language model
+ * would pass IHA_MASK_CAUSAL).  d must be 64 or 128 (IHA_ERR_UNSUPPORTED); B*H at most
+ * 65535 (IHA_ERR_SHAPE).  workspace: device, 256-byte aligned, at least
+ * iha_nexus_inner_workspace() bytes (a channel-major copy of Q and the flag word), else
+ * IHA_ERR_WORKSPACE.  IHA_FLAG_CHECK synchronises and reports an empty row or a
+ * non-finite output.  The products run on fp16 matrix cores with fp32 accumulation (the
+ * probabilities rounded to fp16), like iha_attention. */
+iha_status iha_nexus_inner_workspace(int64_t B, int64_t L, int64_t H, int64_t d, size_t* bytes);
+iha_status iha_nexus_inner(int64_t B, int64_t L, int64_t H, int64_t d, int32_t mask, int64_t window,
+                           float score_scale, const void* Q, float* O, uint32_t flags, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* iha_status_str(iha_status status);
 

@@ -95,6 +95,11 @@ def load_library() -> ctypes.CDLL:
         lib.iha_attention.argtypes = [i64, i64, i64, i64, i32, i64, ctypes.c_float, vp, vp, vp, vp,
                                       u32, vp, vp]
         lib.iha_attention.restype = ctypes.c_int
+        lib.iha_nexus_inner_workspace.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
+        lib.iha_nexus_inner_workspace.restype = ctypes.c_int
+        lib.iha_nexus_inner.argtypes = [i64, i64, i64, i64, i32, i64, ctypes.c_float, vp, vp, u32, vp,
+                                        ctypes.c_size_t, vp]
+        lib.iha_nexus_inner.restype = ctypes.c_int
         lib.iha_attention_backward_workspace.argtypes = [i64, i64, i64, i64, ctypes.POINTER(ctypes.c_size_t)]
         lib.iha_attention_backward_workspace.restype = ctypes.c_int
         lib.iha_attention_backward.argtypes = [i64, i64, i64, i64, i32, i64, ctypes.c_float, vp, vp, vp, vp,
@@ -229,6 +234,37 @@ def iha_forward_static(X, W_Q, W_K, W_V, alpha_Q, alpha_K, alpha_V, R, H: int, P
     st = load_library().iha_forward_static(ctypes.byref(prob), *args, stream)
     if st != IHA_OK:
         raise IHAError(st, "iha_forward_static")
+    return out
+
+
+def iha_nexus_inner(Q, mask_mode="none", window: Optional[int] = None, score_scale: Optional[float] = None,
+                    flags: int = 0, out=None, workspace=None):
+    """Nexus inner attention softmax(Q Q^T / sqrt(d)) Q per head (keys and values are the
+    queries): Q fp16 [B, L, H, d] -> fp32 [B, L, H, d].  score_scale defaults to
+    log2(e)/sqrt(d) (base-2 scores)."""
+    import torch
+    B, L, H, d = (int(s) for s in Q.shape)
+    mask = _mask_code(mask_mode)
+    if window is None:
+        window = 0
+    if score_scale is None:
+        score_scale = math.log2(math.e) / math.sqrt(d)
+    q = _dev_ptr(Q, "Q", torch.float16, (B, L, H, d))
+    lib = load_library()
+    nbytes = ctypes.c_size_t(0)
+    st = lib.iha_nexus_inner_workspace(B, L, H, d, ctypes.byref(nbytes))
+    if st != IHA_OK:
+        raise IHAError(st, "iha_nexus_inner_workspace")
+    if workspace is None:
+        workspace = torch.empty(int(nbytes.value), dtype=torch.uint8, device=Q.device)
+    if out is None:
+        out = torch.empty((B, L, H, d), dtype=torch.float32, device=Q.device)
+    o = _dev_ptr(out, "out", torch.float32, (B, L, H, d))
+    stream = ctypes.c_void_p(torch.cuda.current_stream(Q.device).cuda_stream)
+    st = lib.iha_nexus_inner(B, L, H, d, mask, int(window), float(score_scale), q, o, flags,
+                             ctypes.c_void_p(workspace.data_ptr()), int(workspace.numel()), stream)
+    if st != IHA_OK:
+        raise IHAError(st, "iha_nexus_inner")
     return out
 
 

@@ -472,6 +472,55 @@ iha_status iha_attention(int64_t B, int64_t L, int64_t H, int64_t d, int32_t mas
   return IHA_OK;
 }
 
+iha_status iha_nexus_inner_workspace(int64_t B, int64_t L, int64_t H, int64_t d, size_t* bytes) {
+  if (!bytes) return IHA_ERR_INVALID_ARG;
+  if (B < 1 || L < 1 || H < 1) return IHA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return IHA_ERR_UNSUPPORTED;
+  if (L > kMaxRows || B * H > 65535 || B * L * H * d > kMaxElems / 4) return IHA_ERR_SHAPE;
+  *bytes = kAlign + align_up(static_cast<size_t>(B * L * H * d) * 2);
+  return IHA_OK;
+}
+
+iha_status iha_nexus_inner(int64_t B, int64_t L, int64_t H, int64_t d, int32_t mask, int64_t window,
+                           float score_scale, const void* Q, float* O, uint32_t flags, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  size_t need = 0;
+  const iha_status v = iha_nexus_inner_workspace(B, L, H, d, &need);
+  if (v != IHA_OK) return v;
+  if (mask < IHA_MASK_NONE || mask > IHA_MASK_WINDOW) return IHA_ERR_INVALID_ARG;
+  if (!Q || !O || !(score_scale > 0.f) || !std::isfinite(score_scale)) return IHA_ERR_INVALID_ARG;
+  if (!aligned(Q, 16) || !aligned(O, 16)) return IHA_ERR_INVALID_ARG;
+  if ((flags & ~IHA_FLAG_CHECK) != 0) return IHA_ERR_INVALID_ARG;
+  if (mask == IHA_MASK_WINDOW && window < 1) return IHA_ERR_EMPTY_ROW;
+  if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < need) return IHA_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  unsigned* flag = reinterpret_cast<unsigned*>(ws);
+  auto* Qt = reinterpret_cast<iha::half_t*>(ws + kAlign);
+  IHA_HIP(iha::launch_clear_flag(flag, stream));
+  IHA_HIP(iha::launch_transpose_rows(static_cast<const iha::half_t*>(Q), Qt, static_cast<int>(B), static_cast<int>(L),
+                                     static_cast<int>(H), static_cast<int>(d), stream));
+  iha::AttnArgs at{};
+  at.Q = Q;
+  at.K = Q;
+  at.Vt = Qt;
+  at.O = O;
+  at.flag = flag;
+  at.B = static_cast<int>(B);
+  at.L = static_cast<int>(L);
+  at.H = static_cast<int>(H);
+  at.d = static_cast<int>(d);
+  at.mask = mask;
+  at.window = mask == IHA_MASK_WINDOW ? static_cast<int>(window < L ? window : L) : 0;
+  at.qk_scale = score_scale;
+  IHA_HIP(iha::launch_attn_f16(at, stream));
+  if (flags & IHA_FLAG_CHECK) {
+    IHA_HIP(iha::launch_check_values(O, iha::kValF32, B * L * H * d, flag, iha::kFlagNonFinite,
+                                     __builtin_inff(), stream));
+    return read_flag(flag, stream);
+  }
+  return IHA_OK;
+}
+
 iha_status iha_attention_backward_workspace(int64_t B, int64_t L, int64_t H, int64_t d, size_t* bytes) {
   if (!bytes) return IHA_ERR_INVALID_ARG;
   const iha_status st = bwd_validate(B, L, H, d, IHA_MASK_NONE, 0);

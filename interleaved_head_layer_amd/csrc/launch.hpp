@@ -104,6 +104,9 @@ struct AttnBwdArgs {
   float dk_scale;  // ln 2 (dK is formed from the scaled Q)
 };
 hipError_t launch_attn_bwd(const AttnBwdArgs& a, hipStream_t s);
+
+// Q [B][L][H][d] fp16 -> Qt [B][H][d][L] fp16 (channel-major copy; d a multiple of 64).
+hipError_t launch_transpose_rows(const half_t* Q, half_t* Qt, int B, int L, int H, int d, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t s);
 
 // bf16 projection path: exact bf16 GEMMs (fp32 accumulation) then fp32 mixing.

@@ -8,10 +8,13 @@ benchmark's CPU-baseline leg may import this package; the product path never
 does.  It shares no code with the HIP library.
 
 Functions and the passages they follow:
-  attention(...)  textbook section 5.3, eq. 5.11 and Algorithm 5.1
-  forward(...)    IHA page section 4, Algorithm 1 (mixing, stacking, attention,
-                  collapse, concatenation)
-  param_count()   IHA page, Theorem 2: Q + 4 H^2 P
+  attention(...)    textbook section 5.3, eq. 5.11 and Algorithm 5.1
+  forward(...)      IHA page section 4, Algorithm 1 (mixing, stacking, attention,
+                    collapse, concatenation)
+  nexus_inner(...)  "Higher-order attention mechanisms" page, section 2: the inner
+                    attention softmax(Q Q^T / sqrt(d_k)) Q, per head, each row by
+                    Algorithm 5.1 with the queries as keys and values
+  param_count()     IHA page, Theorem 2: Q + 4 H^2 P
 """
 from __future__ import annotations
 
@@ -133,6 +136,22 @@ def forward(X, WQ, WK, WV, aQ, aK, aV, R, H: int, P: int, mask: int, window: int
     if rc != OK:
         raise OracleError(rc)
     return (out, float(dev[0])) if return_rowsum_dev else out
+
+
+def nexus_inner(Q, mask: int = MASK_NONE, window: int = 0) -> np.ndarray:
+    """Nexus inner attention ("Higher-order attention mechanisms" page, section 2):
+    Attention_q(X) = softmax(Q Q^T / sqrt(d_k)) Q, for Q [B, L, H, d] per (b, h) - the
+    attention of each row over the visible rows of the same Q, which serve as keys and
+    values.  The page's formula has no mask (MASK_NONE); causal and window masks restrict
+    the visible rows as for the IHA forward.  Returns [B, L, H, d] in double."""
+    Q = _f64(Q)
+    B, L, H, d = Q.shape
+    out = np.zeros_like(Q)
+    for b in range(B):
+        for h in range(H):
+            q = np.ascontiguousarray(Q[b, :, h])
+            out[b, :, h], _, _ = attention(q, q, q, mask, window)
+    return out
 
 
 def param_count(D: int, H: int, P: int) -> int:

@@ -75,6 +75,15 @@ int main(void) {
   expect(iha_attention_backward(1, 64, 2, 64, IHA_MASK_WINDOW, 0, 0.1f, fake, fake, fake, fake,
                                 (float*)fake, (float*)fake, (float*)fake, fake, bws, NULL),
          IHA_ERR_EMPTY_ROW, "backward window 0");
+  size_t nws = 0;
+  expect(iha_nexus_inner_workspace(1, 64, 2, 128, &nws), IHA_OK, "nexus workspace");
+  expect(iha_nexus_inner_workspace(1, 64, 2, 96, &nws), IHA_ERR_UNSUPPORTED, "nexus d = 96");
+  expect(iha_nexus_inner(1, 64, 2, 128, IHA_MASK_WINDOW, 0, 0.1f, fake, (float*)fake, 0, fake, nws, NULL),
+         IHA_ERR_EMPTY_ROW, "nexus window 0");
+  expect(iha_nexus_inner(1, 64, 2, 128, IHA_MASK_CAUSAL, 0, 0.1f, fake, (float*)fake, 0, fake, nws - 1, NULL),
+         IHA_ERR_WORKSPACE, "nexus short workspace");
+  expect(iha_nexus_inner(1, 64, 2, 128, IHA_MASK_CAUSAL, 0, 0.1f, fake + 8, (float*)fake, 0, fake, nws, NULL),
+         IHA_ERR_INVALID_ARG, "nexus misaligned Q");
   for (int s = 0; s <= 8; ++s)
     if (!iha_status_str((iha_status)s) || !strncmp(iha_status_str((iha_status)s), "IHA_ERR_UNKNOWN", 15)) {
       fprintf(stderr, "FAIL: no name for status %d\n", s);
