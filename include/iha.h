@@ -1,7 +1,7 @@
 /*
  * iha.h - C ABI of the MI355X (gfx950) library for the forward pass of
- * Interleaved Head Attention (IHA), and for the gradients of its attention step
- * (iha_attention_backward, below).
+ * Interleaved Head Attention (IHA), for the gradients of the layer (iha_backward) and
+ * of its attention step alone (iha_attention_backward, below).
  *
  * What is computed: Algorithm 1 of the "Interleaved Head Attention" page
  * (section 4; arXiv 2602.21371), for one layer and a batch of sequences:
@@ -220,6 +220,40 @@ iha_status iha_attention_backward(int64_t B, int64_t L, int64_t H, int64_t d, in
                                   const void* K, const void* V, const void* dO, float* dQ,
                                   float* dK, float* dV, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
+
+/* Gradients of the whole layer (reverse mode through Algorithm 1 of the "Interleaved
+ * Head Attention" page, section 4: projection, mixing, stacking, attention, collapse),
+ * for the loss L = sum(G * X~) with X~ the output of iha_forward on the same inputs:
+ *   dR[h][h'*P + j]   = sum_t G[t][h] . P-bar_{h'}[t*P + j]
+ *   dP-bar_{h'}[t*P + j] = sum_h R[h][h'*P + j] G[t][h]
+ *   dQ-bar, dK-bar, dV-bar: the attention step's chain rule (textbook "Attention
+ *                       mechanism", eq. 5.3 and 5.11; as in iha_attention_backward)
+ *   dalpha[m][h][j]   = sum_t Y_m[t] . dQ-bar_h[t*P + j]   (and for K, V)
+ *   dY_m[t]           = sum_{h, j} alpha[m][h][j] dQ-bar_h[t*P + j]
+ *   dW = X^T dY (per projection),  dX = sum over Q, K, V of dY W^T
+ * (Y_m: head m of the projection X W; the dot products run over the d channels, the
+ * sums over the B*N tokens).  Inputs as for iha_forward with dtype IHA_BF16 only (else
+ * IHA_ERR_UNSUPPORTED): X [B][N][D] and W_* [D][D] bf16, alpha_* [H][H][P] and
+ * R [H][H*P] float, plus the upstream gradient G float [B][N][D].  Outputs, all float
+ * and caller-allocated: dX [B][N][D], dW_* [D][D], dalpha_* [H][H][P], dR [H][H*P].
+ * Every pointer device memory, 16-byte aligned, else IHA_ERR_INVALID_ARG.  The limits
+ * of iha_forward and iha_attention_backward apply (d = D/H of 64 or 128, P*N stacked
+ * rows), and B*N must be at most 2^21 - 64 (IHA_ERR_SHAPE).  workspace: device, 256-byte
+ * aligned, at least iha_backward_workspace() bytes, else IHA_ERR_WORKSPACE.
+ * Precision: bf16 projections with fp32 accumulation and fp32 mixing, as the forward;
+ * the stacked Q~, K~, V~, dP-bar and the attention's probabilities and dS are fp16
+ * matrix-core operands; the reductions over tokens run in fp32; dY enters the dW and dX
+ * products as bf16 high and low parts (16 significant bits, fp32 accumulation).  Stacked values beyond the fp16 range
+ * become infinite: IHA_FLAG_CHECK synchronises and reports that (IHA_ERR_RANGE), a
+ * non-finite input (IHA_ERR_NONFINITE) or a non-finite gradient.  Without it the call
+ * is enqueued on `stream` and returns without waiting. */
+iha_status iha_backward_workspace(const iha_problem* prob, size_t* bytes);
+iha_status iha_backward(const iha_problem* prob, const void* X, const void* W_Q,
+                        const void* W_K, const void* W_V, const float* alpha_Q,
+                        const float* alpha_K, const float* alpha_V, const float* R,
+                        const float* G, float* dX, float* dW_Q, float* dW_K, float* dW_V,
+                        float* dalpha_Q, float* dalpha_K, float* dalpha_V, float* dR,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* The inner attention of the Nexus higher-order attention ("Higher-order attention
  * mechanisms" page, section 2, the refined query and key: Attention_q(X) =

@@ -105,6 +105,10 @@ def load_library() -> ctypes.CDLL:
         lib.iha_attention_backward.argtypes = [i64, i64, i64, i64, i32, i64, ctypes.c_float, vp, vp, vp, vp,
                                                vp, vp, vp, vp, ctypes.c_size_t, vp]
         lib.iha_attention_backward.restype = ctypes.c_int
+        lib.iha_backward_workspace.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+        lib.iha_backward_workspace.restype = ctypes.c_int
+        lib.iha_backward.argtypes = [P] + [vp] * 18 + [ctypes.c_size_t, vp]
+        lib.iha_backward.restype = ctypes.c_int
         lib.iha_status_str.argtypes = [ctypes.c_int]
         lib.iha_status_str.restype = ctypes.c_char_p
         _lib = lib
@@ -235,6 +239,48 @@ def iha_forward_static(X, W_Q, W_K, W_V, alpha_Q, alpha_K, alpha_V, R, H: int, P
     if st != IHA_OK:
         raise IHAError(st, "iha_forward_static")
     return out
+
+
+def iha_backward_workspace_bytes(prob: iha_problem) -> int:
+    n = ctypes.c_size_t(0)
+    st = load_library().iha_backward_workspace(ctypes.byref(prob), ctypes.byref(n))
+    if st != IHA_OK:
+        raise IHAError(st, "iha_backward_workspace")
+    return n.value
+
+
+def iha_backward(X, W_Q, W_K, W_V, alpha_Q, alpha_K, alpha_V, R, G, H: int, P: int, mask_mode,
+                 window: Optional[int] = None, flags: int = 0, workspace=None):
+    """Gradients of the IHA layer for the loss sum(G * X~) (iha_backward): X [B, N, D] and
+    W_* [D, D] bf16, alpha_* [H, H, P], R [H, H*P] and G [B, N, D] fp32, all on the GPU.
+    Returns a dict of fp32 tensors {"X", "WQ", "WK", "WV", "aQ", "aK", "aV", "R"}."""
+    import torch
+    if X.dim() != 3 or X.dtype != torch.bfloat16:
+        raise TypeError("X must be a bfloat16 [B, N, D] tensor")
+    B, N, D = (int(s) for s in X.shape)
+    H, P = int(H), int(P)
+    prob = make_problem(B, N, D, H, P, mask_mode, window, IHA_BF16, flags)
+    args = [_dev_ptr(X, "X")]
+    for n, w in (("W_Q", W_Q), ("W_K", W_K), ("W_V", W_V)):
+        args.append(_dev_ptr(w, n, torch.bfloat16, (D, D)))
+    for n, a in (("alpha_Q", alpha_Q), ("alpha_K", alpha_K), ("alpha_V", alpha_V)):
+        args.append(_dev_ptr(a, n, torch.float32, (H, H, P)))
+    args.append(_dev_ptr(R, "R", torch.float32, (H, H * P)))
+    args.append(_dev_ptr(G, "G", torch.float32, (B, N, D)))
+    dev = X.device
+    shapes = {"X": (B, N, D), "WQ": (D, D), "WK": (D, D), "WV": (D, D), "aQ": (H, H, P),
+              "aK": (H, H, P), "aV": (H, H, P), "R": (H, H * P)}
+    grads = {k: torch.empty(v, dtype=torch.float32, device=dev) for k, v in shapes.items()}
+    args += [ctypes.c_void_p(grads[k].data_ptr()) for k in shapes]
+    need = iha_backward_workspace_bytes(prob)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    args += [_dev_ptr(workspace, "workspace", torch.uint8), ctypes.c_size_t(workspace.numel())]
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    st = load_library().iha_backward(ctypes.byref(prob), *args, stream)
+    if st != IHA_OK:
+        raise IHAError(st, "iha_backward")
+    return grads
 
 
 def iha_nexus_inner(Q, mask_mode="none", window: Optional[int] = None, score_scale: Optional[float] = None,

@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJDIR = os.path.join(ROOT, "_build", "iha")
 LIB = os.path.join(PKG, "libiha.so")
 SOURCES = ["iha.hip", "fold.hip", "gemm.hip", "proj.hip", "attn.hip", "attn_bwd.hip", "collapse.hip",
-           "nexus.hip"]
+           "nexus.hip", "bwd.hip"]
 # Measurement probe for the benchmark (chip clock and matrix-core rate), a library of its own.
 PROBE_LIB = os.path.join(PKG, "libiha_probe.so")
 PROBE_SOURCES = ["probe.hip"]

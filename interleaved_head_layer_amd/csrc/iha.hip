@@ -359,6 +359,59 @@ iha_status bwd_validate(int64_t B, int64_t L, int64_t H, int64_t d, int32_t mask
   return IHA_OK;
 }
 
+// Workspace of iha_backward (bf16 inputs).  The fp32 projections Y = X [W_Q | W_K | W_V] are
+// kept for the mixing gradient and then overwritten with the projection gradients dY.
+struct LayerBwdLayout {
+  size_t flag, wt, y, qb, kb, vb, dpb, dq, dk, dv, att, part, dycat, dyt, xt, wcat, total;
+  int64_t Mp;  // tokens rounded up to 64 (the K dimension of the weight-gradient GEMM)
+  BwdLayout a;
+};
+
+LayerBwdLayout layer_bwd_layout(const iha_problem& p) {
+  LayerBwdLayout l{};
+  const size_t M = static_cast<size_t>(p.B) * p.N, D = static_cast<size_t>(p.D);
+  const size_t act = M * p.P * D;  // elements of each stacked tensor
+  l.Mp = (static_cast<int64_t>(M) + 63) / 64 * 64;
+  l.a = bwd_layout(p.B, p.P * p.N, p.H, p.D / p.H);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  l.flag = take(kAlign);
+  l.wt = take(3 * D * D * 2);
+  l.y = take(M * 3 * D * 4);
+  l.qb = take(act * 2);
+  l.kb = take(act * 2);
+  l.vb = take(act * 2);
+  l.dpb = take(act * 2);
+  l.dq = take(act * 4);
+  l.dk = take(act * 4);
+  l.dv = take(act * 4);
+  l.att = take(l.a.total);
+  l.part = take(iha::head_reduce_part_bytes(static_cast<int>(M), static_cast<int>(p.H), static_cast<int>(p.P)));
+  // bf16 high and low parts of dY (token-major [M][6D]: high 3D then low 3D; channel-major
+  // [3D][2Mp]: high Mp then low Mp), X^T twice ([D][2Mp]) and [W_Q | W_K | W_V] twice ([D][6D]).
+  l.dycat = take(M * 6 * D * 2);
+  l.dyt = take(3 * D * 2 * static_cast<size_t>(l.Mp) * 2);
+  l.xt = take(D * 2 * static_cast<size_t>(l.Mp) * 2);
+  l.wcat = take(D * 6 * D * 2);
+  l.total = off;
+  return l;
+}
+
+iha_status layer_bwd_validate(const iha_problem* p) {
+  const iha_status v = validate(p);
+  if (v != IHA_OK) return v;
+  if (p->dtype != IHA_BF16) return IHA_ERR_UNSUPPORTED;
+  const iha_status a = bwd_validate(p->B, p->P * p->N, p->H, p->D / p->H, p->mask, p->window);
+  if (a != IHA_OK) return a;
+  // The weight-gradient GEMM reads 256 rows of 2*Mp bf16 values per tile: under 2 GiB.
+  if ((p->B * p->N + 63) / 64 * 64 * 2 * 2 * 256 >= (int64_t{1} << 31)) return IHA_ERR_SHAPE;
+  return IHA_OK;
+}
+
 // Workspace of iha_forward_static: one copy per device, held until the process ends.  In
 // host code `scratch` names a host-side stand-in, never the device memory: host code uses
 // only the per-device address that hipGetSymbolAddress returns for it.
@@ -571,6 +624,185 @@ iha_status iha_attention_backward(int64_t B, int64_t L, int64_t H, int64_t d, in
   a.dq_scale = score_scale * 0.69314718055994531f;
   a.dk_scale = 0.69314718055994531f;
   IHA_HIP(iha::launch_attn_bwd(a, stream));
+  return IHA_OK;
+}
+
+iha_status iha_backward_workspace(const iha_problem* prob, size_t* bytes) {
+  if (!bytes) return IHA_ERR_INVALID_ARG;
+  const iha_status v = layer_bwd_validate(prob);
+  if (v != IHA_OK) return v;
+  *bytes = layer_bwd_layout(*prob).total;
+  return IHA_OK;
+}
+
+iha_status iha_backward(const iha_problem* prob, const void* X, const void* W_Q, const void* W_K,
+                        const void* W_V, const float* alpha_Q, const float* alpha_K, const float* alpha_V,
+                        const float* R, const float* G, float* dX, float* dW_Q, float* dW_K, float* dW_V,
+                        float* dalpha_Q, float* dalpha_K, float* dalpha_V, float* dR, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  const iha_status v = layer_bwd_validate(prob);
+  if (v != IHA_OK) return v;
+  const void* ins[] = {X, W_Q, W_K, W_V, alpha_Q, alpha_K, alpha_V, R, G};
+  const void* outs[] = {dX, dW_Q, dW_K, dW_V, dalpha_Q, dalpha_K, dalpha_V, dR};
+  for (const void* q : ins)
+    if (!q || !aligned(q, 16)) return IHA_ERR_INVALID_ARG;
+  for (const void* q : outs)
+    if (!q || !aligned(q, 16)) return IHA_ERR_INVALID_ARG;
+  const iha_problem& p = *prob;
+  const LayerBwdLayout lay = layer_bwd_layout(p);
+  if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < lay.total) return IHA_ERR_WORKSPACE;
+  using iha::half_t;
+  char* ws = static_cast<char*>(workspace);
+  unsigned* flag = reinterpret_cast<unsigned*>(ws + lay.flag);
+  const int B = static_cast<int>(p.B), N = static_cast<int>(p.N), D = static_cast<int>(p.D);
+  const int H = static_cast<int>(p.H), P = static_cast<int>(p.P), d = D / H, M = B * N, L = P * N;
+  const int64_t act = static_cast<int64_t>(M) * P * D;
+  float* Y = reinterpret_cast<float*>(ws + lay.y);
+  auto* Qb = reinterpret_cast<half_t*>(ws + lay.qb);
+  auto* Kb = reinterpret_cast<half_t*>(ws + lay.kb);
+  auto* Vb = reinterpret_cast<half_t*>(ws + lay.vb);
+  auto* dPb = reinterpret_cast<half_t*>(ws + lay.dpb);
+  float* dBar[3] = {reinterpret_cast<float*>(ws + lay.dq), reinterpret_cast<float*>(ws + lay.dk),
+                    reinterpret_cast<float*>(ws + lay.dv)};
+  float* part = reinterpret_cast<float*>(ws + lay.part);
+  auto* dYcat = reinterpret_cast<uint16_t*>(ws + lay.dycat);
+  auto* dYt = reinterpret_cast<uint16_t*>(ws + lay.dyt);
+  auto* Xt = reinterpret_cast<uint16_t*>(ws + lay.xt);
+  auto* Wcat = reinterpret_cast<uint16_t*>(ws + lay.wcat);
+  const float* alphas[3] = {alpha_Q, alpha_K, alpha_V};
+  float* dalphas[3] = {dalpha_Q, dalpha_K, dalpha_V};
+  float* dWs[3] = {dW_Q, dW_K, dW_V};
+  const uint16_t* Ws[3] = {static_cast<const uint16_t*>(W_Q), static_cast<const uint16_t*>(W_K),
+                           static_cast<const uint16_t*>(W_V)};
+  if (log_enabled())
+    std::fprintf(stderr, "[iha] backward B=%d N=%d D=%d H=%d d=%d P=%d mask=%d window=%lld\n", B, N, D, H, d, P,
+                 p.mask, static_cast<long long>(p.window));
+
+  // Forward steps 1-2 again: Y = X W (kept in fp32) and the mixed, stacked Q~, K~, V~ (fp16).
+  iha::ProjArgs pa{};
+  pa.X = static_cast<const uint16_t*>(X);
+  for (int w = 0; w < 3; ++w) {
+    pa.W[w] = Ws[w];
+    pa.alpha[w] = alphas[w];
+  }
+  pa.Wt = reinterpret_cast<uint16_t*>(ws + lay.wt);
+  pa.Yqk = Y;
+  pa.Q = Qb;
+  pa.K = Kb;
+  pa.Vrow = Vb;
+  pa.B = B;
+  pa.N = N;
+  pa.D = D;
+  pa.H = H;
+  pa.d = d;
+  pa.P = P;
+  pa.qscale = 1.f;
+  pa.flag = flag;  // cleared by the weight transpose
+  IHA_HIP(iha::launch_proj_rowmajor(pa, stream));
+
+  // Collapse (steps 4-5) in reverse: dR = sum over tokens of G (x) P-bar, and the stacked
+  // outputs' gradient dP-bar[t*P + j][h'] = sum_h R[h][h'*P + j] G[t][h].
+  IHA_HIP(iha::launch_expand(G, R, dPb, B, N, H, P, d, stream));
+
+  // Attention (step 3) in reverse; it recomputes the fp16 forward output P-bar on the way.
+  const BwdLayout& al = lay.a;
+  char* aws = ws + lay.att;
+  iha::AttnBwdArgs a{};
+  a.Q = Qb;
+  a.K = Kb;
+  a.V = Vb;
+  a.dO = dPb;
+  a.dQ = dBar[0];
+  a.dK = dBar[1];
+  a.dV = dBar[2];
+  a.Qs = reinterpret_cast<half_t*>(aws + al.qs);
+  a.QsT = reinterpret_cast<half_t*>(aws + al.qst);
+  a.KT = reinterpret_cast<half_t*>(aws + al.kt);
+  a.dOT = reinterpret_cast<half_t*>(aws + al.dot);
+  a.VT = reinterpret_cast<half_t*>(aws + al.vt);
+  a.O = reinterpret_cast<half_t*>(aws + al.o);
+  a.lse = reinterpret_cast<float*>(aws + al.lse);
+  a.D = reinterpret_cast<float*>(aws + al.dd);
+  a.B = B;
+  a.L = L;
+  a.H = H;
+  a.d = d;
+  a.mask = p.mask;
+  a.window = p.mask == IHA_MASK_WINDOW ? static_cast<int>(p.window < L ? p.window : L) : 0;
+  a.Lp = static_cast<int>(al.Lp);
+  a.scale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(d)));
+  a.dq_scale = a.scale * 0.69314718055994531f;
+  a.dk_scale = 0.69314718055994531f;
+  IHA_HIP(iha::launch_attn_bwd(a, stream));
+  IHA_HIP(iha::launch_head_reduce(G, D, a.O, true, dR, part, M, H, P, d, stream));
+
+  // Mixing (step 2) in reverse: dalpha[m][h][j] = sum over tokens of Y_m (x) dBar_{h,j}, and
+  // dY_m = sum_{h,j} alpha[m][h][j] dBar_{h,j} - a collapse with alpha in place of R.  The dY
+  // go where Y was (after the last reduction that reads Y), then to bf16 high and low parts
+  // (rounding dY to bf16 alone costs about 2^-9 of the largest gradients): token-major for dX,
+  // channel-major for dW.
+  const int64_t D3 = 3 * static_cast<int64_t>(D), Mp = lay.Mp;
+  for (int w = 0; w < 3; ++w)
+    IHA_HIP(iha::launch_head_reduce(Y + static_cast<int64_t>(w) * D, D3, dBar[w], false, dalphas[w], part, M, H, P,
+                                    d, stream));
+  for (int w = 0; w < 3; ++w) {
+    float* dY = Y + static_cast<int64_t>(w) * M * D;
+    IHA_HIP(iha::launch_collapse(dBar[w], alphas[w], dY, M, H, P, d, stream));
+    IHA_HIP(iha::launch_to_bf16(dY, D, M, D, dYcat + w * D, dYcat + D3 + w * D, 2 * D3, stream));
+    uint16_t* t = dYt + static_cast<int64_t>(w) * D * 2 * Mp;
+    IHA_HIP(iha::launch_to_bf16_t(dY, false, D, M, D, t, t + Mp, 2 * Mp, Mp, stream));
+    for (int half = 0; half < 2; ++half)
+      IHA_HIP(iha::launch_copy_bf16(Ws[w], D, D, D, Wcat + half * D3 + w * D, 2 * D3, stream));
+  }
+
+  // Projection (step 1) in reverse: dW_m = X^T (dY_m high + low) as one product over 2 Mp
+  // tokens, dX = sum_m (dY_m high + low) W_m^T as one product over 6D.
+  for (int half = 0; half < 2; ++half)
+    IHA_HIP(iha::launch_to_bf16_t(X, true, D, M, D, Xt + half * Mp, nullptr, 2 * Mp, Mp, stream));
+  for (int w = 0; w < 3; ++w) {
+    iha::NtArgs g{};
+    g.A = Xt;
+    g.B = dYt + static_cast<int64_t>(w) * D * 2 * Mp;
+    g.C = dWs[w];
+    g.I = D;
+    g.J = D;
+    g.K = static_cast<int>(2 * Mp);
+    g.ldc = D;
+    IHA_HIP(iha::launch_gemm_nt_bf16(g, stream));
+  }
+  iha::NtArgs g{};
+  g.A = dYcat;
+  g.B = Wcat;
+  g.C = dX;
+  g.I = M;
+  g.J = D;
+  g.K = static_cast<int>(2 * D3);
+  g.ldc = D;
+  IHA_HIP(iha::launch_gemm_nt_bf16(g, stream));
+
+  if (p.flags & IHA_FLAG_CHECK) {
+    // Non-finite inputs; stacked fp16 tensors beyond the fp16 range; non-finite gradients.
+    using iha::kFlagInputNonFinite;
+    const float inf = __builtin_inff();
+    const int64_t nx = static_cast<int64_t>(M) * D, nw = static_cast<int64_t>(D) * D;
+    const int64_t na = static_cast<int64_t>(H) * H * P;
+    IHA_HIP(iha::launch_check_values(X, iha::kValBF16, nx, flag, kFlagInputNonFinite, inf, stream));
+    IHA_HIP(iha::launch_check_values(G, iha::kValF32, nx, flag, kFlagInputNonFinite, inf, stream));
+    for (int w = 0; w < 3; ++w) {
+      IHA_HIP(iha::launch_check_values(Ws[w], iha::kValBF16, nw, flag, kFlagInputNonFinite, inf, stream));
+      IHA_HIP(iha::launch_check_values(alphas[w], iha::kValF32, na, flag, kFlagInputNonFinite, inf, stream));
+    }
+    IHA_HIP(iha::launch_check_values(R, iha::kValF32, na, flag, kFlagInputNonFinite, inf, stream));
+    for (const half_t* t : {Qb, Kb, Vb, dPb})
+      IHA_HIP(iha::launch_check_values(t, iha::kValF16, act, flag, iha::kFlagRange, inf, stream));
+    IHA_HIP(iha::launch_check_values(dX, iha::kValF32, nx, flag, iha::kFlagNonFinite, inf, stream));
+    for (int w = 0; w < 3; ++w) {
+      IHA_HIP(iha::launch_check_values(dWs[w], iha::kValF32, nw, flag, iha::kFlagNonFinite, inf, stream));
+      IHA_HIP(iha::launch_check_values(dalphas[w], iha::kValF32, na, flag, iha::kFlagNonFinite, inf, stream));
+    }
+    IHA_HIP(iha::launch_check_values(dR, iha::kValF32, na, flag, iha::kFlagNonFinite, inf, stream));
+    return read_flag(flag, stream);
+  }
   return IHA_OK;
 }
 

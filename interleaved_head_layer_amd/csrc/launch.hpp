@@ -137,6 +137,8 @@ struct ProjArgs {
   int T0;                 // ceil(R / P): tokens whose pseudo-tokens include a first row
   float qscale;           // factor applied to the fp16 Q (the base-2 score scale)
   unsigned* flag;         // status word, cleared by the first kernel (may be null)
+  int ywidth;             // projected matrices per token row of Yqk (0: 2, Q and K)
+  half_t* Vrow;           // launch_proj_rowmajor: V~ [B][P*N][H][d] fp16 (row-major)
 };
 // With P = 4 the fused epilogue writes four stacked outputs per projected value and its
 // stores no longer hide behind the products (measured: slower than GEMM + mixing), so the
@@ -151,6 +153,37 @@ bool proj_fused(const ProjArgs& pa);
 // ev_prep (may be null) is recorded after the weight transpose, ev_gemm after the projection
 // GEMMs (with the fused path: after the fused kernel, the mixing included).
 hipError_t launch_proj_bf16(const ProjArgs& pa, hipStream_t s, hipEvent_t ev_prep, hipEvent_t ev_gemm);
+// Projections and mixing for the backward pass: W transposed into Wt, Y = X [Wt_Q; Wt_K;
+// Wt_V]^T into Yqk ([B*N][3D] fp32, kept: the mixing gradient needs it), and the mixed Q~, K~,
+// V~ row-major into Q, K, Vrow ([B][P*N][H][d] fp16, Q~ times qscale).  R must be 0.
+hipError_t launch_proj_rowmajor(ProjArgs pa, hipStream_t s);
+// C[I][ldc] = A[I][K] B[J][K]^T, bf16 operands (K a multiple of 64), fp32 result.
+hipError_t launch_gemm_nt_bf16(const NtArgs& g, hipStream_t s);
+// The gradient of the collapse with respect to the stacked outputs:
+//   out[b][t*P + j][h'][c] = sum_h R[h][h'*P + j] * G[b][t][h*d + c]
+// G fp32 [B*N][H*d] (16-byte aligned), out fp16 [B][N*P][H][d].
+hipError_t launch_expand(const float* G, const float* Rm, half_t* out, int B, int N, int H, int P, int d,
+                         hipStream_t s);
+
+// Token reduction of the mixing and collapse gradients:
+//   out[a][h*P + j] = sum_t sum_c A[t*lda + a*d + c] * Bm[((t*P + j)*H + h)*d + c]
+// over ntok tokens; A fp32, Bm fp32 or fp16 (b_half).  Per-chunk partial sums go to `part`
+// (head_reduce_part_bytes() bytes), then a second kernel adds them in a fixed order.
+size_t head_reduce_part_bytes(int ntok, int H, int P);
+hipError_t launch_head_reduce(const float* A, int64_t lda, const void* Bm, bool b_half, float* out, float* part,
+                              int ntok, int H, int P, int d, hipStream_t s);
+// dst[r*ldd + c] = hi = bf16(src[r*lds + c]) for r < nr, c < nc (nc a multiple of 4), src
+// fp32; dst_lo (may be null) gets bf16(src - hi) at the same offsets.
+hipError_t launch_to_bf16(const float* src, int64_t lds, int nr, int nc, uint16_t* dst, uint16_t* dst_lo, int64_t ldd,
+                          hipStream_t s);
+// dst[c*ldd + r] = bf16(src[r*lds + c]) for c < nc and r < nr_out, zero for r >= nr; src fp32
+// (src_bf16 false) or bf16 bits; dst_lo (may be null) as above.  nr <= nr_out <= ldd, nr_out a
+// multiple of 64.
+hipError_t launch_to_bf16_t(const void* src, bool src_bf16, int64_t lds, int nr, int nc, uint16_t* dst,
+                            uint16_t* dst_lo, int64_t ldd, int64_t nr_out, hipStream_t s);
+// dst[r*ldd + c] = src[r*lds + c], bf16 bits, for r < nr, c < nc (nc a multiple of 8).
+hipError_t launch_copy_bf16(const uint16_t* src, int64_t lds, int nr, int nc, uint16_t* dst, int64_t ldd,
+                            hipStream_t s);
 
 
 // Unstack + collapse + concatenation:

@@ -517,9 +517,10 @@ __global__ __launch_bounds__(256) void mix_qk_kernel(ProjArgs pa) {
   const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (e >= static_cast<int64_t>(pa.B) * N * groups) return;
   const int tok = static_cast<int>(e / groups), c = static_cast<int>(e % groups) * CW;
-  const float* __restrict__ y = pa.Yqk + static_cast<int64_t>(tok) * 2 * D + which * D + c;
-  half_t* __restrict__ out = (which == 0 ? pa.Q : pa.K) + static_cast<int64_t>(tok) * P * D + c;
-  float* __restrict__ oute = which == 0 ? pa.Qe : pa.Ke;
+  const int yw = pa.ywidth > 0 ? pa.ywidth : 2;  // projected matrices per token row of Yqk
+  const float* __restrict__ y = pa.Yqk + static_cast<int64_t>(tok) * yw * D + which * D + c;
+  half_t* __restrict__ out = (which == 0 ? pa.Q : which == 1 ? pa.K : pa.Vrow) + static_cast<int64_t>(tok) * P * D + c;
+  float* __restrict__ oute = which == 0 ? pa.Qe : which == 1 ? pa.Ke : nullptr;
   const float oscale = which == 0 ? pa.qscale : 1.f;  // Q leaves pre-scaled, in one rounding
   const int b = tok / N, t = tok % N;
   float ym[HMAX][CW];
@@ -775,7 +776,69 @@ void launch_mix(const ProjArgs& pa, hipStream_t s) {
   hipLaunchKernelGGL((mix_v_kernel<HMAX, TW>), dim3(static_cast<unsigned>((nv + 255) / 256), pa.d), dim3(256), lds, s, pa);
 }
 
+template <int HMAX>
+void launch_mix_rows(const ProjArgs& pa, int nmat, hipStream_t s) {
+  constexpr int CW = HMAX <= 20 ? 4 : HMAX <= 32 ? 2 : 1;
+  const int64_t M = static_cast<int64_t>(pa.B) * pa.N;
+  const size_t lds = static_cast<size_t>(pa.H) * pa.P * HMAX * sizeof(float);
+  const int64_t n = M * (pa.d / CW);
+  hipLaunchKernelGGL((mix_qk_kernel<HMAX, CW>), dim3(static_cast<unsigned>((n + 255) / 256), nmat), dim3(256), lds, s,
+                     pa);
+}
+
 }  // namespace
+
+hipError_t launch_gemm_nt_bf16(const NtArgs& g, hipStream_t s) { return launch_gemm_nt(g, s); }
+
+hipError_t launch_expand(const float* G, const float* Rm, half_t* out, int B, int N, int H, int P, int d,
+                         hipStream_t s) {
+  // The mixing kernel with G as the only projected matrix and R as the coefficients: R's
+  // [h][h'*P + j] layout is the mixing coefficients' [m][h][j] with m = h.
+  ProjArgs pa{};
+  pa.alpha[0] = Rm;
+  pa.Yqk = const_cast<float*>(G);
+  pa.ywidth = 1;
+  pa.Q = out;
+  pa.qscale = 1.f;
+  pa.B = B;
+  pa.N = N;
+  pa.D = H * d;
+  pa.H = H;
+  pa.P = P;
+  pa.d = d;
+  if (H <= 4) launch_mix_rows<4>(pa, 1, s);
+  else if (H <= 8) launch_mix_rows<8>(pa, 1, s);
+  else if (H <= 16) launch_mix_rows<16>(pa, 1, s);
+  else if (H <= 20) launch_mix_rows<20>(pa, 1, s);
+  else if (H <= 32) launch_mix_rows<32>(pa, 1, s);
+  else launch_mix_rows<64>(pa, 1, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_proj_rowmajor(ProjArgs pa, hipStream_t s) {
+  const int D = pa.D, M = pa.B * pa.N;
+  if (!pa.Vrow || pa.R != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(wprep_kernel, dim3(D / 64, D / 64, 3), dim3(256), 0, s, pa, 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  NtArgs g{};  // Y = X * [Wt_Q; Wt_K; Wt_V]^T, token-major [M][3D]
+  g.A = pa.X;
+  g.B = pa.Wt;
+  g.C = pa.Yqk;
+  g.I = M;
+  g.J = 3 * D;
+  g.K = D;
+  g.ldc = 3 * D;
+  if ((e = launch_gemm_nt(g, s)) != hipSuccess) return e;
+  pa.ywidth = 3;
+  if (pa.H <= 4) launch_mix_rows<4>(pa, 3, s);
+  else if (pa.H <= 8) launch_mix_rows<8>(pa, 3, s);
+  else if (pa.H <= 16) launch_mix_rows<16>(pa, 3, s);
+  else if (pa.H <= 20) launch_mix_rows<20>(pa, 3, s);
+  else if (pa.H <= 32) launch_mix_rows<32>(pa, 3, s);
+  else launch_mix_rows<64>(pa, 3, s);
+  return hipGetLastError();
+}
 
 bool proj_fused(const ProjArgs& pa) { return fused_shape(pa.H, pa.D, pa.P); }
 

@@ -190,6 +190,13 @@ def make_stacked_grad(B: int, PN: int, H: int, d: int, seed: int) -> np.ndarray:
     return rng.standard_normal((B, PN, H, d), dtype=np.float32).astype(np.float16).astype(np.float32)
 
 
+def make_output_grad(w: Workload) -> np.ndarray:
+    """Draw an upstream gradient G of the layer output, [B, N, D] float32, N(0, 1), from PCG64
+    seeded with (seed, 98)."""
+    rng = np.random.Generator(np.random.PCG64([w.seed, 98]))
+    return rng.standard_normal((w.B, w.N, w.D), dtype=np.float32)
+
+
 def sample_tokens(w: Workload, n: int, seed: int = 0) -> np.ndarray:
     """Flat token indices b*N + t to check at full size: the first and last tokens of each
     sequence (fewest / most visible keys) plus uniformly drawn ones, sorted and unique."""

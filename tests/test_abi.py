@@ -192,3 +192,38 @@ def test_attention_backward_workspace_and_validation():
     assert lib.iha_attention_backward(*args(0, 0, 1.0, qp=odd)) == bd.STATUS_NAMES.index("IHA_ERR_INVALID_ARG")
     assert lib.iha_attention_backward(*args(1, 0, 1.0, ws=odd)) == bd.STATUS_NAMES.index("IHA_ERR_WORKSPACE")
     assert lib.iha_attention_backward(*args(1, 0, 1.0, nb=16)) == bd.STATUS_NAMES.index("IHA_ERR_WORKSPACE")
+
+
+def test_layer_backward_workspace_and_validation():
+    """Host-side checks of iha_backward, which return before any launch: bf16 only, the
+    attention backward's head widths, null or misaligned pointers, a short workspace."""
+    lib = bd.load_library()
+    code = bd.STATUS_NAMES.index
+    n = ctypes.c_size_t(0)
+    p = bd.make_problem(2, 100, 256, 2, 2, "causal")
+    assert lib.iha_backward_workspace(ctypes.byref(p), ctypes.byref(n)) == bd.IHA_OK
+    M, D, act = 200, 256, 200 * 2 * 256
+    # at least: transposed W, fp32 Y, four fp16 and three fp32 stacked tensors, bf16 high and
+    # low dY (token- and channel-major), X^T twice and the concatenated W twice
+    Mp = 256
+    assert n.value >= (3 * D * D * 2 + M * 3 * D * 4 + 4 * act * 2 + 3 * act * 4 + M * 6 * D * 2
+                       + 3 * D * 2 * Mp * 2 + D * 2 * Mp * 2 + D * 6 * D * 2)
+    pf = bd.make_problem(2, 100, 256, 2, 2, "causal", dtype=bd.IHA_F32)
+    assert lib.iha_backward_workspace(ctypes.byref(pf), ctypes.byref(n)) == code("IHA_ERR_UNSUPPORTED")
+    p96 = bd.make_problem(1, 64, 192, 2, 2, "causal")
+    assert lib.iha_backward_workspace(ctypes.byref(p96), ctypes.byref(n)) == code("IHA_ERR_UNSUPPORTED")
+    pw = bd.make_problem(1, 64, 128, 2, 2, "window", 0)
+    assert lib.iha_backward_workspace(ctypes.byref(pw), ctypes.byref(n)) == code("IHA_ERR_EMPTY_ROW")
+    assert lib.iha_backward_workspace(ctypes.byref(p), None) == code("IHA_ERR_INVALID_ARG")
+    fake = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 8)
+    big = ctypes.c_size_t(1 << 40)
+    ptrs = [fake] * 17   # X, W_Q, W_K, W_V, alpha_Q/K/V, R, G, then the eight gradients
+    for k in range(17):
+        a = list(ptrs)
+        a[k] = None
+        assert lib.iha_backward(ctypes.byref(p), *a, fake, big, None) == code("IHA_ERR_INVALID_ARG"), k
+        a[k] = odd
+        assert lib.iha_backward(ctypes.byref(p), *a, fake, big, None) == code("IHA_ERR_INVALID_ARG"), k
+    assert lib.iha_backward(ctypes.byref(p), *ptrs, fake, ctypes.c_size_t(16), None) == code("IHA_ERR_WORKSPACE")
+    assert lib.iha_backward(ctypes.byref(p), *ptrs, odd, big, None) == code("IHA_ERR_WORKSPACE")
