@@ -14,8 +14,8 @@ dominant kernel and of every kernel, a pass of K steps each preceded by a 512 Mi
 that flushes the caches (median of those steps), the matrix-core rate and shader clock the
 chip sustains under a pure-product load (libiha_probe.so), the CPU oracle timed on a bounded
 token sample with the GPU output checked against it on those tokens, the same figures for
-the other full-size workloads (fewer steps), and the attention backward at the 4 x 4096-token
-workload's attention shape.
+the other full-size workloads (fewer steps), the attention backward at the 4 x 4096-token
+workload's attention shape, and the layer backward (all gradients) at the headline shapes.
 
 Work per unit (algorithmic, the count the pages' convention gives):
   attention  4 * d flops per visible (query, key) pair: QK^T and AV at 2 flops per
@@ -355,6 +355,54 @@ def run_nexus_inner(B, L, H, d, mask, steps, warmup):
             "note": "whole call: the channel-major copy of Q and the attention kernel"}
 
 
+def run_layer_backward(w, steps, warmup):
+    """Time iha_backward (the layer's gradients dX, dW, dalpha, dR) on workload `w`, inputs
+    resident on the GPU.  Work counted: the projections recomputed, dW and dX at 6 * D^2 flops
+    per token each (the high/low split of dY doubles the executed products of the last two,
+    not the algorithmic count), and the attention backward at 2.5x the forward's 4 * d flops
+    per visible pair; the mixing, collapse and reductions over tokens are not counted."""
+    import torch
+    import interleaved_head_layer_amd as iha
+
+    B, N, D, H, P, d = w.B, w.N, w.D, w.H, w.P, w.D // w.H
+    mask = ["none", "causal", "window"][w.mask]
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(4321)
+    rnd = lambda *shape, s=1.0: torch.randn(shape, generator=g, device=dev) * s
+    X = rnd(B, N, D).bfloat16()
+    Ws = [rnd(D, D, s=D ** -0.5).bfloat16() for _ in range(3)]
+    als = [rnd(H, H, P, s=H ** -0.5) for _ in range(3)]
+    R = rnd(H, H * P, s=(H * P) ** -0.5)
+    G = rnd(B, N, D)
+    prob = iha.make_problem(B, N, D, H, P, mask, w.window)
+    ws = torch.empty(iha.iha_backward_workspace_bytes(prob), dtype=torch.uint8, device=dev)
+    call = lambda: iha.iha_backward(X, *Ws, *als, R, G, H, P, mask, w.window, workspace=ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    gemm = 3 * 6.0 * D * D * B * N
+    att = 2.5 * 4.0 * d * B * H * allowed_pairs(P * N, w.mask, w.window)
+    out = {"shape": {"B": B, "N": N, "D": D, "H": H, "d": d, "P": P, "mask": mask, "window": w.window},
+           "ms": round(ms, 4), "steps": steps, "work_flop": gemm + att,
+           "gemm_flop": gemm, "attention_flop": att,
+           "tokens_per_s": round(B * N / (ms * 1e-3), 1),
+           "roofline": roof("mfma", gemm + att, ms),
+           "workspace_bytes": int(ws.numel()),
+           "note": "whole call: projections and mixing recomputed, expand through R, attention "
+                   "backward, token reductions for dalpha and dR, collapse for dY, dW and dX GEMMs"}
+    del X, Ws, als, R, G, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -369,6 +417,8 @@ def main():
     ap.add_argument("--extra-steps", type=int, default=5)
     ap.add_argument("--only-backward", action="store_true",
                     help="time only the attention backward of the workload's attention shape")
+    ap.add_argument("--only-layer-backward", action="store_true",
+                    help="time only the layer backward (iha_backward) of the workload")
     ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (reference for HBM counters)")
     args = ap.parse_args()
@@ -393,6 +443,12 @@ def main():
         print(json.dumps({"workload": w.name,
                           "attention_backward": run_attention_backward(w, args.steps, args.warmup)}),
               flush=True)
+        return
+
+    if args.only_layer_backward:
+        for n in ([args.workload] if args.workload else list(HEADLINE)):
+            print(json.dumps({"workload": n, "layer_backward": run_layer_backward(wl.WORKLOADS[n], args.steps,
+                                                                                  args.warmup)}), flush=True)
         return
 
     names = [args.workload] if args.workload else list(HEADLINE)
@@ -429,7 +485,7 @@ def main():
                           "tokens' elements (the test suite compares whole outputs)"}
     fw.free()
 
-    extra, bwd = {}, None
+    extra, bwd, layer_bwd = {}, None, None
     if not args.no_extra:
         for name in OTHERS:
             if name in names:
@@ -455,6 +511,7 @@ def main():
         bwd = run_attention_backward(wl.WORKLOADS[OTHERS[0]], args.extra_steps, 3)
         extra["nexus_inner_causal_b4_l8192_h16"] = run_nexus_inner(4, 8192, 16, 128, "causal",
                                                                    args.extra_steps, 3)
+        layer_bwd = {n: run_layer_backward(wl.WORKLOADS[n], args.extra_steps, 2) for n in HEADLINE}
 
     chip = probe_chip()
     if chip is not None:
@@ -484,6 +541,7 @@ def main():
         "chip": chip,
         "other_workloads": extra,
         "attention_backward": bwd,
+        "layer_backward": layer_bwd,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

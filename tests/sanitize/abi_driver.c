@@ -84,6 +84,20 @@ int main(void) {
          IHA_ERR_WORKSPACE, "nexus short workspace");
   expect(iha_nexus_inner(1, 64, 2, 128, IHA_MASK_CAUSAL, 0, 0.1f, fake + 8, (float*)fake, 0, fake, nws, NULL),
          IHA_ERR_INVALID_ARG, "nexus misaligned Q");
+  size_t lws = 0;
+  float* ff = (float*)fake;
+  expect(iha_backward_workspace(&p, &lws), IHA_OK, "layer backward workspace");
+  q = p; q.dtype = IHA_F32;
+  expect(iha_backward_workspace(&q, &lws), IHA_ERR_UNSUPPORTED, "layer backward fp32");
+  expect(iha_backward(&p, fake, fake, fake, fake, af, af, af, af, af, ff, ff, ff, ff, ff, ff, ff, ff, fake,
+                      lws - 1, NULL),
+         IHA_ERR_WORKSPACE, "layer backward short workspace");
+  expect(iha_backward(&p, fake, fake, fake, fake, af, af, af, af, NULL, ff, ff, ff, ff, ff, ff, ff, ff, fake,
+                      lws, NULL),
+         IHA_ERR_INVALID_ARG, "layer backward null G");
+  expect(iha_backward(&p, fake, fake, fake, fake, af, af, af, af, af, ff, ff, ff, ff, ff, ff, ff, ff + 2, fake,
+                      lws, NULL),
+         IHA_ERR_INVALID_ARG, "layer backward misaligned dR");
   for (int s = 0; s <= 8; ++s)
     if (!iha_status_str((iha_status)s) || !strncmp(iha_status_str((iha_status)s), "IHA_ERR_UNKNOWN", 15)) {
       fprintf(stderr, "FAIL: no name for status %d\n", s);

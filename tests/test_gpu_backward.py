@@ -115,3 +115,87 @@ def test_layer_backward_rejects_f32(progress):
     with pytest.raises(iha.IHAError) as e:
         iha.iha_backward_workspace_bytes(prob)
     assert e.value.status == 6  # IHA_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------------ full size
+# At the full sizes the oracle cannot form whole-layer gradients (dR, dalpha and dW sum over
+# every token; in causal mode every gradient depends on the whole sequence).  Two checks hold
+# there instead:
+#  * exact identities of the layer's structure, for L = sum(G * X~) with X~ from iha_forward:
+#    X~ is linear in R, in alpha_V and in W_V, so <dR, R> = <dalpha_V, alpha_V> =
+#    <dW_V, W_V> = L; the scores are unchanged by alpha_Q * c, alpha_K / c (and by W_Q * c,
+#    W_K / c), and Q~ is linear in both W_Q and alpha_Q, so <dalpha_Q, alpha_Q> =
+#    <dalpha_K, alpha_K> = <dW_Q, W_Q> = <dW_K, W_K>; every projection is linear in X, so
+#    <dX, X> = sum over Q, K, V of <dW, W>.  A transposed, dropped or mis-scaled gradient
+#    breaks one of them by order one.  Bar: 1e-3 of the sum of the terms' magnitudes.
+#  * under the window mask a token's dX depends only on the tokens within one window on either
+#    side (its stacked rows see keys back to W_s - 1 positions; the queries that see them lie
+#    within W_s - 1 positions after, and their own keys start no earlier): the oracle's
+#    backward on that sub-sequence gives those tokens' dX exactly.
+FULL = ["iha_window_p2_b4_n4096", "iha_window_p4_b2_n8192_wide", "iha_causal_p4_b2_n8192_wide"]
+ID_TOL = 1e-3
+
+
+def _upload(x, G):
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV).bfloat16()
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+    t = {k: bf(x[k]) for k in ("X", "WQ", "WK", "WV")}
+    t.update({k: f32(x[k]) for k in ("aQ", "aK", "aV", "R")})
+    t["G"] = f32(G)
+    return t
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_layer_backward_full_size_identities(name, progress):
+    w = wl.WORKLOADS[name]
+    progress(f"layer backward identities {w.describe()}")
+    x = wl.make_inputs(w)
+    G = wl.make_output_grad(w)
+    t = _upload(x, G)
+    args = [t[k] for k in ("X", "WQ", "WK", "WV", "aQ", "aK", "aV", "R")]
+    out = iha.iha_forward(*args, w.H, w.P, ["none", "causal", "window"][w.mask], w.window)
+    g = iha.iha_backward(*args, t["G"], w.H, w.P, ["none", "causal", "window"][w.mask], w.window)
+    torch.cuda.synchronize()
+    dot = lambda a, b: float((a.double() * b.double()).sum())
+    mag = lambda a, b: float((a.double() * b.double()).abs().sum())
+    L, Lmag = dot(t["G"], out), mag(t["G"], out)
+    pairs = {"R": (g["R"], t["R"]), "aV": (g["aV"], t["aV"]), "WV": (g["WV"], t["WV"]),
+             "aQ": (g["aQ"], t["aQ"]), "aK": (g["aK"], t["aK"]), "WQ": (g["WQ"], t["WQ"]),
+             "WK": (g["WK"], t["WK"]), "X": (g["X"], t["X"])}
+    v = {k: dot(a, b) for k, (a, b) in pairs.items()}
+    m = {k: mag(a, b) for k, (a, b) in pairs.items()}
+    v["L"], m["L"] = L, Lmag
+    v["W"] = v["WQ"] + v["WK"] + v["WV"]
+    m["W"] = m["WQ"] + m["WK"] + m["WV"]
+    progress(" ".join(f"{k}={v[k]:.6g}" for k in v))
+    for a, b in [("R", "L"), ("aV", "L"), ("WV", "L"), ("aQ", "aK"), ("WQ", "aQ"), ("WK", "aK"),
+                 ("X", "W")]:
+        scale = m[a] + m[b]
+        rel = abs(v[a] - v[b]) / scale
+        note(f"{name}: <d{a},{a}> = {v[a]:.6g} vs {b} = {v[b]:.6g}: |diff| / scale = {rel:.3e}")
+        assert rel <= ID_TOL, (a, b, rel)
+
+
+@pytest.mark.parametrize("name", ["iha_window_p2_b4_n4096", "iha_window_p4_b2_n8192_wide"])
+def test_layer_backward_full_size_window_tokens(name, progress):
+    w = wl.WORKLOADS[name]
+    assert w.mask == wl.MASK_WINDOW
+    x = wl.make_inputs(w)
+    G = wl.make_output_grad(w)
+    t = _upload(x, G)
+    args = [t[k] for k in ("X", "WQ", "WK", "WV", "aQ", "aK", "aV", "R")]
+    g = iha.iha_backward(*args, t["G"], w.H, w.P, "window", w.window)
+    torch.cuda.synchronize()
+    dX = g["X"].cpu().numpy().astype(np.float64)
+    del g, t
+    torch.cuda.empty_cache()
+    margin = -(-w.window // w.P)   # whole tokens covering W_s stacked positions
+    b = w.B - 1
+    for t0 in (w.N // 2, margin + 3):
+        t1 = t0 + 4
+        s, e = t0 - margin, min(w.N, t1 + margin)
+        assert s >= 0
+        progress(f"{name}: oracle backward on tokens {s}..{e - 1} of sequence {b} for dX of {t0}..{t1 - 1}")
+        ref = bw.forward_and_grads(x["X"][b:b + 1, s:e], x["WQ"], x["WK"], x["WV"], x["aQ"], x["aK"],
+                                   x["aV"], x["R"], w.H, w.P, w.mask, w.window, G[b:b + 1, s:e])["X"]
+        check(dX[b, t0:t1], ref[0, t0 - s:t1 - s], f"{name} dX tokens {t0}..{t1 - 1}")
