@@ -243,10 +243,11 @@ iha_status iha_attention_backward(int64_t B, int64_t L, int64_t H, int64_t d, in
  * Precision: bf16 projections with fp32 accumulation and fp32 mixing, as the forward;
  * the stacked Q~, K~, V~, dP-bar and the attention's probabilities and dS are fp16
  * matrix-core operands; the reductions over tokens run in fp32; dY enters the dW and dX
- * products as bf16 high and low parts (16 significant bits, fp32 accumulation).  Stacked values beyond the fp16 range
- * become infinite: IHA_FLAG_CHECK synchronises and reports that (IHA_ERR_RANGE), a
- * non-finite input (IHA_ERR_NONFINITE) or a non-finite gradient.  Without it the call
- * is enqueued on `stream` and returns without waiting. */
+ * products as bf16 high and low parts (16 significant bits, fp32 accumulation).
+ * Stacked values beyond the fp16 range become infinite: IHA_FLAG_CHECK synchronises
+ * and reports that (IHA_ERR_RANGE), a non-finite input (IHA_ERR_NONFINITE) or a
+ * non-finite gradient.  Without it the call is enqueued on `stream` and returns
+ * without waiting. */
 iha_status iha_backward_workspace(const iha_problem* prob, size_t* bytes);
 iha_status iha_backward(const iha_problem* prob, const void* X, const void* W_Q,
                         const void* W_K, const void* W_V, const float* alpha_Q,
