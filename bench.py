@@ -136,10 +136,10 @@ class Forwards:
         self.out = torch.empty((w0.B, w0.N, w0.D), dtype=torch.float32, device=dev)
         self.fused = [bool(iha.iha_plan(p) & iha.IHA_PLAN_MIX_FUSED) for p in self.probs]
 
-    def forward(self, i, events=None):
+    def forward(self, i, events=None, flags=0):
         w = self.ws_list[i]
         self.iha.iha_forward(*self.args, w.H, w.P, w.mask, w.window, out=self.out, workspace=self.ws,
-                             events=events)
+                             events=events, flags=flags)
 
     def step(self):
         for i in range(len(self.ws_list)):
@@ -355,6 +355,33 @@ def run_nexus_inner(B, L, H, d, mask, steps, warmup):
             "note": "whole call: the channel-major copy of Q and the attention kernel"}
 
 
+def run_fused_collapse_ab(w, steps):
+    """A/B of the collapse placement on workload `w`: whole forwards with the separate collapse
+    kernel (default) against IHA_FLAG_FUSED_COLLAPSE (the collapse in the attention epilogue
+    with fp32 atomics), `steps` each after 2 warm-up forwards, alternating twice."""
+    import torch
+    fw = Forwards([w])
+    res = {"default": [], "fused_collapse": []}
+    for _ in range(2):
+        for name, flags in (("default", 0), ("fused_collapse", fw.iha.IHA_FLAG_FUSED_COLLAPSE)):
+            for _ in range(2):
+                fw.forward(0, flags=flags)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                fw.forward(0, flags=flags)
+            e1.record()
+            torch.cuda.synchronize()
+            res[name].append(e0.elapsed_time(e1) / steps)
+    fw.free()
+    d, f = min(res["default"]), min(res["fused_collapse"])
+    return {"workload": w.name, "ms_per_forward_default": round(d, 4), "ms_per_forward_fused_collapse": round(f, 4),
+            "fused_over_default": round(f / d, 2), "steps": steps,
+            "note": "whole forwards; the fused collapse zeroes X~ and adds every stacked output row, "
+                    "weighted by R, into all H output heads with fp32 atomics from the attention epilogue"}
+
+
 def run_layer_backward(w, steps, warmup):
     """Time iha_backward (the layer's gradients dX, dW, dalpha, dR) on workload `w`, inputs
     resident on the GPU.  Work counted: the projections recomputed, dW and dX at 6 * D^2 flops
@@ -419,6 +446,8 @@ def main():
                     help="time only the attention backward of the workload's attention shape")
     ap.add_argument("--only-layer-backward", action="store_true",
                     help="time only the layer backward (iha_backward) of the workload")
+    ap.add_argument("--only-fused-collapse", action="store_true",
+                    help="time only the collapse-placement A/B of the workload")
     ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (reference for HBM counters)")
     args = ap.parse_args()
@@ -443,6 +472,11 @@ def main():
         print(json.dumps({"workload": w.name,
                           "attention_backward": run_attention_backward(w, args.steps, args.warmup)}),
               flush=True)
+        return
+
+    if args.only_fused_collapse:
+        for n in ([args.workload] if args.workload else [OTHERS[0], HEADLINE[0]]):
+            print(json.dumps({"fused_collapse_ab": run_fused_collapse_ab(wl.WORKLOADS[n], args.steps)}), flush=True)
         return
 
     if args.only_layer_backward:
@@ -512,6 +546,8 @@ def main():
         extra["nexus_inner_causal_b4_l8192_h16"] = run_nexus_inner(4, 8192, 16, 128, "causal",
                                                                    args.extra_steps, 3)
         layer_bwd = {n: run_layer_backward(wl.WORKLOADS[n], args.extra_steps, 2) for n in HEADLINE}
+        extra["fused_collapse_ab"] = [run_fused_collapse_ab(wl.WORKLOADS[n], 3)
+                                      for n in (OTHERS[0], HEADLINE[0])]
 
     chip = probe_chip()
     if chip is not None:

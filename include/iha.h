@@ -101,6 +101,16 @@ typedef enum { IHA_F32 = 0, IHA_BF16 = 1 } iha_dtype;
 
 /* Synchronise and report device-detected problems (see "Errors"). */
 #define IHA_FLAG_CHECK 1u
+/* IHA_BF16 only (else IHA_ERR_UNSUPPORTED): steps 4-5 of Algorithm 1 (unstack, collapse with
+ * R, concatenation) run in the attention kernel's epilogue instead of a kernel of their own:
+ * X_out is zeroed, then every stacked output row of head h' adds R[h][h'*P + j] times itself
+ * into X_out[t][h] for every head h, with fp32 atomic additions.  The result equals the
+ * default path's to rounding (the atomics' order varies, so it is not bitwise reproducible).
+ * It exists to measure the fused design against the default: each attention workgroup holds
+ * one head's outputs while the collapse mixes all heads of a token, so every output element
+ * takes H*P atomic additions from different workgroups, and the fused forward measured
+ * about 100x slower than the attention plus the separate collapse kernel. */
+#define IHA_FLAG_FUSED_COLLAPSE 2u
 
 typedef struct {
   int64_t B;       /* batch size, >= 1 */

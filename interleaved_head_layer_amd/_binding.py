@@ -19,6 +19,7 @@ STATUS_NAMES = ["IHA_OK", "IHA_ERR_INVALID_ARG", "IHA_ERR_SHAPE", "IHA_ERR_EMPTY
 IHA_MASK_NONE, IHA_MASK_CAUSAL, IHA_MASK_WINDOW = 0, 1, 2
 IHA_F32, IHA_BF16 = 0, 1
 IHA_FLAG_CHECK = 1
+IHA_FLAG_FUSED_COLLAPSE = 2   # collapse in the attention epilogue (fp32 atomics); for measurement
 IHA_PLAN_MIX_FUSED = 1
 TIMED_EVENTS = 7       # IHA_TIMED_EVENTS in include/iha.h
 STATIC_WORKSPACE_BYTES = 64 << 20   # IHA_STATIC_WORKSPACE_BYTES in include/iha.h

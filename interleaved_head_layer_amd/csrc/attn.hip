@@ -406,7 +406,15 @@ __device__ __forceinline__ void first_rows(const AttnArgs& a, int b, int h, floa
 #pragma unroll
     for (int u = 0; u < CU; ++u) acc[u] = fmaf(p, vs[n][g + EGroup * u], acc[u]);
   }
-  if (r < R) {
+  if (r < R && a.Xf) {  // fused collapse (see the tiled kernel's epilogue)
+    const int P = a.P, t = r / P, j = r % P;
+    float* xrow = a.Xf + (static_cast<int64_t>(b) * (a.L / P) + t) * D;
+    for (int hh = 0; hh < H; ++hh) {
+      const float cf = a.Rm[(hh * H + h) * P + j] * inv;
+#pragma unroll
+      for (int u = 0; u < CU; ++u) atomicAdd(xrow + hh * DH + g + EGroup * u, cf * acc[u]);
+    }
+  } else if (r < R) {
     float* dst = a.Pe + static_cast<int64_t>(b) * a.R2 * D + static_cast<int64_t>(r) * D + h * DH;
 #pragma unroll
     for (int u = 0; u < CU; ++u) dst[g + EGroup * u] = acc[u] * inv;
@@ -533,7 +541,24 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
       if (a.flag) atomicOr(a.flag, kFlagEmptyRow);
     }
     const int64_t orow = obase + static_cast<int64_t>(qrow) * rs;
-    if (qrow >= a.R && qrow < a.R2) {  // early rows with fp32 outputs: [B][R2][H][d]
+    if (a.Xf) {
+      // Fused collapse: X~[b][t][hh*d + c] += R[hh][h*P + j] * O[t*P + j][c] for every head hh
+      // (rows < R come from the fp32 first-row workgroups).
+      if (qrow >= a.R) {
+        const int P = a.P, t = qrow / P, j = qrow % P;
+        float* xrow = a.Xf + (static_cast<int64_t>(b) * (L / P) + t) * rs;
+        for (int hh = 0; hh < H; ++hh) {
+          const float cf = a.Rm[(hh * H + h) * P + j] * inv;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                atomicAdd(xrow + hh * DH + cb * 32 + 8 * q + 4 * hf + e, cf * st.o[cb][4 * q + e]);
+        }
+      }
+    } else if (qrow >= a.R && qrow < a.R2) {  // early rows with fp32 outputs: [B][R2][H][d]
       float* dst = a.Pe + (static_cast<int64_t>(b) * a.R2 + qrow) * rs + h * DH;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)

@@ -115,6 +115,23 @@ hipError_t launch_fold_f32(const FoldArgs& a, hipStream_t s) {
   return launch_fold_impl<float, float>(a, s);
 }
 
+namespace {
+__global__ __launch_bounds__(256) void fill_zero_kernel(floatx4* __restrict__ p, int64_t n4) {
+  const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4; i += static_cast<int64_t>(gridDim.x) * 256)
+    p[i] = z;
+}
+}  // namespace
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
+  if (n % 4 != 0) return hipErrorInvalidValue;
+  const int64_t n4 = n / 4;
+  if (n4 < 1) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(std::max<int64_t>(1, std::min<int64_t>((n4 + 255) / 256, 256 * 8))));
+  hipLaunchKernelGGL(fill_zero_kernel, grid, dim3(256), 0, s, reinterpret_cast<floatx4*>(p), n4);
+  return hipGetLastError();
+}
+
 hipError_t launch_clear_flag(unsigned* flag, hipStream_t s) {
   hipLaunchKernelGGL(clear_flag_kernel, dim3(1), dim3(1), 0, s, flag);
   return hipGetLastError();

@@ -38,8 +38,9 @@ iha_status validate(const iha_problem* p) {
   if (p->B < 1 || p->N < 1 || p->D < 1 || p->H < 1 || p->P < 1) return IHA_ERR_INVALID_ARG;
   if (p->mask < IHA_MASK_NONE || p->mask > IHA_MASK_WINDOW) return IHA_ERR_INVALID_ARG;
   if (p->dtype != IHA_F32 && p->dtype != IHA_BF16) return IHA_ERR_INVALID_ARG;
-  if ((p->flags & ~IHA_FLAG_CHECK) != 0 || p->reserved != 0) return IHA_ERR_INVALID_ARG;
+  if ((p->flags & ~(IHA_FLAG_CHECK | IHA_FLAG_FUSED_COLLAPSE)) != 0 || p->reserved != 0) return IHA_ERR_INVALID_ARG;
   if (p->D % p->H != 0) return IHA_ERR_SHAPE;
+  if ((p->flags & IHA_FLAG_FUSED_COLLAPSE) && p->dtype != IHA_BF16) return IHA_ERR_UNSUPPORTED;
   if (p->H > kMaxH || p->H * p->H * p->P > 16384) return IHA_ERR_UNSUPPORTED;
   if (!d_supported(p->dtype, p->D / p->H)) return IHA_ERR_UNSUPPORTED;
   if (p->dtype == IHA_BF16) {
@@ -277,6 +278,12 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
       at.T0 = (lay.R + P - 1) / P;
       at.escale = score_scale;
     }
+    if (p.flags & IHA_FLAG_FUSED_COLLAPSE) {
+      IHA_HIP(iha::launch_fill_zero(X_out, static_cast<int64_t>(B) * N * D, stream));
+      at.Xf = X_out;
+      at.Rm = R;
+      at.P = P;
+    }
     IHA_HIP(iha::launch_attn_f16(at, stream));
   } else {
     at.O = reinterpret_cast<float*>(ws + lay.pbar);
@@ -285,12 +292,15 @@ iha_status forward_impl(const iha_problem* prob, const void* X, const void* W_Q,
   if (ev) IHA_HIP(hipEventRecord(ev[4], stream));
   if (ev) IHA_HIP(hipEventRecord(ev[5], stream));  // (first rows: part of the attention launch)
 
-  // Steps 4-5: unstack, collapse with R, concatenate heads.
-  if (bf16)
-    IHA_HIP(iha::launch_collapse_h(at.Oh, lay.R2 > 0 ? reinterpret_cast<const float*>(ws + lay.pe) : nullptr,
-                                   lay.R2, R, X_out, B, N, H, P, d, stream));
-  else
-    IHA_HIP(iha::launch_collapse(at.O, R, X_out, B * N, H, P, d, stream));
+  // Steps 4-5: unstack, collapse with R, concatenate heads (with the fused collapse the
+  // attention launch has done them).
+  if (!(p.flags & IHA_FLAG_FUSED_COLLAPSE)) {
+    if (bf16)
+      IHA_HIP(iha::launch_collapse_h(at.Oh, lay.R2 > 0 ? reinterpret_cast<const float*>(ws + lay.pe) : nullptr,
+                                     lay.R2, R, X_out, B, N, H, P, d, stream));
+    else
+      IHA_HIP(iha::launch_collapse(at.O, R, X_out, B * N, H, P, d, stream));
+  }
   if (ev) IHA_HIP(hipEventRecord(ev[6], stream));
 
   if (p.flags & IHA_FLAG_CHECK) {

@@ -74,8 +74,16 @@ struct AttnArgs {
   // fp16 kernel: when set, [B][H][L] base-2 log-sum-exp of every row's visible scores
   // (the row's probabilities are exp2(score - lse)); +inf for a row with no visible key.
   float* lse;
+  // fp16 kernel, fused collapse (when set): X~ [B][L/P][H*d] fp32, zeroed beforehand; every
+  // output row i = t*P + j of head h adds Rm[hh][h*P + j] * O[i] into X~[t][hh*d ..] for every
+  // head hh (fp32 atomics) instead of being stored; rows < R from the fp32 first-row
+  // workgroups.  Needs P.
+  float* Xf;
+  const float* Rm;  // R [H][H*P]
 };
 hipError_t launch_attn_f16(const AttnArgs& a, hipStream_t s);
+// p[0..n) = 0 (n a multiple of 4, p 16-byte aligned); a kernel, so that it may be captured.
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 
 // Attention backward over stacked rows (fp16 operands, fp32 gradients).  Inputs Q, K, V, dO
 // and outputs dQ, dK, dV are row-major [B][L][H][d]; the rest is workspace the launcher fills:

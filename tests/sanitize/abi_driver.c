@@ -35,6 +35,9 @@ int main(void) {
   q = p; q.N = 0; expect(iha_workspace_bytes(&q, &ws), IHA_ERR_INVALID_ARG, "N = 0");
   q = p; q.flags = 0x80; expect(iha_workspace_bytes(&q, &ws), IHA_ERR_INVALID_ARG, "unknown flag");
   q = p; q.reserved = 1; expect(iha_workspace_bytes(&q, &ws), IHA_ERR_INVALID_ARG, "reserved field");
+  q = p; q.flags = IHA_FLAG_FUSED_COLLAPSE; expect(iha_workspace_bytes(&q, &ws), IHA_OK, "fused collapse flag");
+  q.dtype = IHA_F32; q.D = 64; q.H = 4;
+  expect(iha_workspace_bytes(&q, &ws), IHA_ERR_UNSUPPORTED, "fused collapse with fp32 inputs");
   q = p; q.mask = 3; expect(iha_plan(&q, &plan), IHA_ERR_INVALID_ARG, "unknown mask");
   q = p; q.dtype = 5; expect(iha_plan(&q, &plan), IHA_ERR_INVALID_ARG, "unknown dtype");
   q = p; q.B = (int64_t)1 << 40; expect(iha_plan(&q, &plan), IHA_ERR_SHAPE, "too many tokens");

@@ -227,3 +227,17 @@ def test_layer_backward_workspace_and_validation():
         assert lib.iha_backward(ctypes.byref(p), *a, fake, big, None) == code("IHA_ERR_INVALID_ARG"), k
     assert lib.iha_backward(ctypes.byref(p), *ptrs, fake, ctypes.c_size_t(16), None) == code("IHA_ERR_WORKSPACE")
     assert lib.iha_backward(ctypes.byref(p), *ptrs, odd, big, None) == code("IHA_ERR_WORKSPACE")
+
+
+def test_fused_collapse_flag_validation():
+    """IHA_FLAG_FUSED_COLLAPSE is accepted for bf16 problems and rejected for fp32 ones; other
+    unknown flag bits stay invalid."""
+    code = bd.STATUS_NAMES.index
+    st, n_fused = _ws(flags=bd.IHA_FLAG_FUSED_COLLAPSE)
+    assert st == bd.IHA_OK
+    st, n_plain = _ws()
+    assert n_fused == n_plain
+    st, _ = _ws(D=64, H=4, dtype=bd.IHA_F32, flags=bd.IHA_FLAG_FUSED_COLLAPSE)
+    assert st == code("IHA_ERR_UNSUPPORTED")
+    st, _ = _ws(flags=4)
+    assert st == code("IHA_ERR_INVALID_ARG")

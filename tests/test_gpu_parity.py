@@ -327,6 +327,38 @@ def test_collapse_map_beyond_fp16_range():
                   what=f"{w.name} R[1][2] = 1e5")
 
 
+FUSED_COLLAPSE = [
+    # B, N, D, H, P, mask: the plain and fused-mixing paths, every mask, P 1-4, H up to 20
+    (1, 300, 256, 2, 2, "window"),
+    (2, 128, 1024, 16, 2, "causal"),   # mixing fused into the GEMM (fp32 first rows from Ye)
+    (1, 200, 1280, 10, 4, "none"),
+    (1, 100, 2560, 20, 4, "causal"),
+    (1, 64, 512, 4, 1, "window"),
+]
+
+
+@pytest.mark.parametrize("B,N,D,H,P,mask", FUSED_COLLAPSE)
+def test_fused_collapse_option(B, N, D, H, P, mask):
+    """IHA_FLAG_FUSED_COLLAPSE (the collapse in the attention epilogue, fp32 atomics): the same
+    bar against the oracle, and agreement with the default path to rounding."""
+    w = wl.custom(B, N, D, H, P, mask, seed=400 + N + P)
+    note(w.describe() + " fused collapse")
+    x = wl.make_inputs(w)
+    ref = oracle_forward(w, x)
+    fused = gpu_forward(w, x, flags=iha.IHA_FLAG_FUSED_COLLAPSE)
+    check(fused, ref, BF16_TOL, what=w.name + " fused collapse vs oracle")
+    check(fused, gpu_forward(w, x), BF16_TOL, rms=float(np.sqrt(np.mean(ref ** 2))),
+          what=w.name + " fused collapse vs default path")
+
+
+def test_fused_collapse_rejects_fp32():
+    w = wl.WORKLOADS["tiny_f32_none"]
+    x = wl.make_inputs(w)
+    with pytest.raises(iha.IHAError) as e:
+        gpu_forward(w, x, flags=iha.IHA_FLAG_FUSED_COLLAPSE)
+    assert e.value.status == 6  # IHA_ERR_UNSUPPORTED
+
+
 def test_empty_window_is_rejected():
     w = wl.custom(1, 3, 128, 1, 2, "window", seed=3)   # N // (2P) = 0
     assert w.window == 0
