@@ -36,6 +36,8 @@ constexpr int Pad = 8;      // fp16 padding per LDS row (keeps 16-byte rows, spr
 // layout the next product takes as its contracted (B operand) dimension.
 __device__ __forceinline__ int sigma(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
 
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 template <int V>
 struct Slot {
   static constexpr int value = V;
@@ -430,13 +432,224 @@ __global__ __launch_bounds__(BThreads) void bwd_dkdv_kernel(AttnBwdArgs a) {
   }
 }
 
+// dV and dK with the query tiles copied straight from global memory into LDS (buffer loads
+// that write LDS, no staging registers), as two kernels so that each fits two or more
+// workgroups per CU (several waves per SIMD hide one another's latency): one workgroup's
+// registers cannot hold both the dV and the dK accumulators (128 per lane at d = 128) next to
+// the K and V fragments.  PART 0 computes dV = A^T dO (needs the scores: Q rows and K), PART 1
+// dK = dS^T Q (needs the scores and dA = dO V^T: Q and dO rows, K and V); both recompute the
+// scores.  LDS rows are unpadded with XOR-swizzled 16-byte chunks:
+//   Q*scale and dO rows [32][DH]: chunk c of row r at c ^ rswz(r) (the score products read rows
+//     sigma(l) of 16 lanes: the swizzle spreads them over 16 bank groups);
+//   (Q*scale)^T and dO^T [DH][32]: 64-byte rows, chunk c of row r at c ^ ((r >> 2) & 3).
+template <int DH>
+__device__ __forceinline__ int rswz(int r) {
+  return DH == 128 ? ((r & 7) | (((r >> 4) & 1) << 3)) : (r & 7);
+}
+__device__ __forceinline__ int tswz(int r) { return (r >> 2) & 3; }
+
+template <int DH, int PART>
+struct SplitSmem {
+  half_t q[2][QTile * DH];                // Q*scale rows
+  half_t g[2][PART ? QTile * DH : 8];     // dO rows (dK only)
+  half_t t[2][DH * QTile];                // dO^T (dV) or (Q*scale)^T (dK)
+  float ls[2][QTile], ds[2][QTile];       // 16-byte aligned: the arrays above are multiples of 16 bytes
+};
+
+template <int DH, int MASK, int PART>
+__device__ __forceinline__ void bwd_split_body(const AttnBwdArgs& a, SplitSmem<DH, PART>& sm) {
+  constexpr int NKS = DH / 16, NCB = DH / 32, CH = DH / 8;
+  constexpr int RR = QTile * CH / BThreads;  // copy rounds of the row tiles (1 or 2)
+  constexpr int TR = DH * 4 / BThreads;      // copy rounds of the transposed tile (1 or 2)
+  static_assert(RR * BThreads == QTile * CH && TR * BThreads == DH * 4, "tile split");
+  const int L = a.L, H = a.H, window = a.window, Lp = a.Lp;
+  const int nkt = (L + KRows - 1) / KRows;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lid / nkt, kti = lid % nkt;
+  const int b = bh / H, h = bh % H, k0 = kti * KRows;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t rs = static_cast<int64_t>(H) * DH;
+  const int64_t rbase = static_cast<int64_t>(b) * L * rs + h * DH;
+  const int64_t tbase = static_cast<int64_t>(b * H + h) * DH * Lp;
+  const int64_t sbase = static_cast<int64_t>(b * H + h) * L;
+  const int kw0 = k0 + 32 * w, krow = kw0 + l32, kload = min(krow, L - 1);
+
+  // Buffer resources: rows of head h (rows >= L read zero) and the padded channel-major copy.
+  const int rbytes = static_cast<int>(((static_cast<int64_t>(L) - 1) * rs + DH) * 2);
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(a.Qs + rbase),
+                                                                        static_cast<short>(0), rbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(a.dO + rbase),
+                                                                        static_cast<short>(0), rbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<half_t*>((PART ? a.QsT : a.dOT) + tbase), static_cast<short>(0), DH * Lp * 2, 0x00020000);
+  // Per-lane byte offsets within a tile: LDS chunk P = (round * 4 + w) * 64 + lane holds row
+  // P / CH, logical chunk (P % CH) ^ rswz(row) (row tiles), or row P / 4, chunk (P % 4) ^
+  // tswz(row) (the transposed tile).
+  unsigned roff[RR], toff[TR];
+#pragma unroll
+  for (int p = 0; p < RR; ++p) {
+    const int P = (p * BWaves + w) * 64 + lane, r = P / CH, c = (P % CH) ^ rswz<DH>(r);
+    roff[p] = static_cast<unsigned>((r * rs + c * 8) * 2);
+  }
+#pragma unroll
+  for (int p = 0; p < TR; ++p) {
+    const int P = (p * BWaves + w) * 64 + lane, r = P / 4, c = (P % 4) ^ tswz(r);
+    toff[p] = static_cast<unsigned>((static_cast<int64_t>(r) * Lp + c * 8) * 2);
+  }
+  auto issue = [&](int q0, int st) {
+    const unsigned rso = static_cast<unsigned>(q0 * rs * 2), tso = static_cast<unsigned>(q0 * 2);
+#pragma unroll
+    for (int p = 0; p < RR; ++p) {
+      const int ld = (p * BWaves + w) * 512;  // halves
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (__attribute__((address_space(3))) void*)(sm.q[st] + ld), 16,
+                                               roff[p], rso, 0, 0);
+      if (PART)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(grs, (__attribute__((address_space(3))) void*)(sm.g[st] + ld), 16,
+                                                 roff[p], rso, 0, 0);
+    }
+#pragma unroll
+    for (int p = 0; p < TR; ++p) {
+      const int ld = (p * BWaves + w) * 512;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(trs, (__attribute__((address_space(3))) void*)(sm.t[st] + ld), 16,
+                                               toff[p], tso, 0, 0);
+    }
+  };
+
+  half8 kf[NKS], vf[PART ? NKS : 1];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    const int64_t off = rbase + static_cast<int64_t>(kload) * rs + (2 * s + hf) * 8;
+    kf[s] = *reinterpret_cast<const half8*>(a.K + off);
+    if (PART) vf[s] = *reinterpret_cast<const half8*>(a.V + off);
+  }
+  floatx16 acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+
+  int qlo = 0, qhi = L;
+  if (MASK != kMaskNone) qlo = k0;
+  if (MASK == kMaskWindow) qhi = min(L, k0 + KRows - 1 + window);
+  const int qt0 = qlo / QTile, qt1 = (qhi + QTile - 1) / QTile;
+  // lse and D of the next tile's queries pass through registers (rows >= L: +inf and 0, so
+  // that a masked pair's values stay finite).
+  float pl = 0.f, pd = 0.f;
+  auto load_ld = [&](int q0) {
+    if (tid < QTile) {
+      const int q = q0 + tid;
+      pl = q < L ? a.lse[sbase + q] : __builtin_inff();
+      if (PART) pd = q < L ? a.D[sbase + q] : 0.f;
+    }
+  };
+  if (qt0 < qt1) {
+    issue(qt0 * QTile, 0);
+    load_ld(qt0 * QTile);
+  }
+  wait_vmem();
+  if (tid < QTile) {
+    sm.ls[0][tid] = pl;
+    sm.ds[0][tid] = pd;
+  }
+  __syncthreads();
+  const int qr = sigma(l32);
+  for (int qti = qt0; qti < qt1; ++qti) {
+    const int q0 = qti * QTile, st = (qti - qt0) & 1;
+    const bool more = qti + 1 < qt1;
+    if (more) {
+      issue(q0 + QTile, st ^ 1);
+      load_ld(q0 + QTile);
+    }
+    bool act = true, edge = q0 + QTile > L || kw0 + 32 > L;
+    if (MASK != kMaskNone) {
+      act = kw0 <= q0 + QTile - 1;
+      edge |= kw0 + 31 > q0;
+    }
+    if (MASK == kMaskWindow) {
+      act = act && (q0 < kw0 + 31 + window);
+      edge |= q0 + QTile - 1 >= kw0 + window;
+    }
+    if (act) {
+      floatx16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+      for (int k = 0; k < NKS; ++k) {
+        const int off = qr * DH + ((2 * k + hf) ^ rswz<DH>(qr)) * 8;
+        s = mfma32(*reinterpret_cast<const half8*>(sm.q[st] + off), kf[k], s);
+        if (PART) dp = mfma32(*reinterpret_cast<const half8*>(sm.g[st] + off), vf[k], dp);
+      }
+      // Lane (l32, hf), accumulator r: key krow, query q0 + 16*hf + r.  PART 0 keeps the
+      // probabilities, PART 1 dS = A * (dA - D).
+      half8 pf[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = 16 * hf + r;
+        float v = fast_exp2(s[r] - sm.ls[st][qi]);
+        if (PART) v *= dp[r] - sm.ds[st][qi];
+        if (edge && !seen<MASK>(q0 + qi, krow, L, window)) v = 0.f;
+        pf[r >> 3][r & 7] = static_cast<half_t>(v);
+      }
+      // dV^T += dO^T A  or  dK^T += (Q*scale)^T dS.
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int c = cb * 32 + l32, off = c * QTile + ((2 * hf + s2) ^ tswz(c)) * 8;
+          acc[cb] = mfma32(*reinterpret_cast<const half8*>(sm.t[st] + off), pf[s2], acc[cb]);
+        }
+    }
+    wait_vmem();
+    if (more && tid < QTile) {
+      sm.ls[st ^ 1][tid] = pl;
+      sm.ds[st ^ 1][tid] = pd;
+    }
+    __syncthreads();
+  }
+  if (krow < L) {
+    float* dst = (PART ? a.dK : a.dV) + rbase + static_cast<int64_t>(krow) * rs;
+    const float sc = PART ? a.dk_scale : 1.f;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        floatx4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[cb][4 * q4 + e] * sc;
+        *reinterpret_cast<floatx4*>(dst + cb * 32 + 8 * q4 + 4 * hf) = v;
+      }
+  }
+}
+
+// dV: about 150-160 registers at d = 128, three workgroups per CU; dK: about 200, two.
+template <int DH, int MASK>
+__global__ __launch_bounds__(BThreads, 3) void bwd_dv_kernel(AttnBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) SplitSmem<DH, 0> sm;
+  bwd_split_body<DH, MASK, 0>(a, sm);
+}
+template <int DH, int MASK>
+__global__ __launch_bounds__(BThreads, 2) void bwd_dk_kernel(AttnBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) SplitSmem<DH, 1> sm;
+  bwd_split_body<DH, MASK, 1>(a, sm);
+}
+
 template <int DH, int MASK>
 hipError_t launch_grads(const AttnBwdArgs& a, hipStream_t s) {
   const int nqt = (a.L + QRows - 1) / QRows, nkt = (a.L + KRows - 1) / KRows;
   hipLaunchKernelGGL((bwd_dq_kernel<DH, MASK>), dim3(nqt * a.H * a.B), dim3(BThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<DH, MASK>), dim3(nkt * a.H * a.B), dim3(BThreads), 0, s, a);
+  // Direct tile copies need 32-bit byte offsets within one (b, h)'s rows and channel-major copy.
+  const bool direct = static_cast<int64_t>(a.L) * a.H * DH * 2 < (int64_t{1} << 31) &&
+                      static_cast<int64_t>(DH) * a.Lp * 2 < (int64_t{1} << 31);
+  if (direct) {
+    hipLaunchKernelGGL((bwd_dv_kernel<DH, MASK>), dim3(nkt * a.H * a.B), dim3(BThreads), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dk_kernel<DH, MASK>), dim3(nkt * a.H * a.B), dim3(BThreads), 0, s, a);
+  } else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<DH, MASK>), dim3(nkt * a.H * a.B), dim3(BThreads), 0, s, a);
   return hipGetLastError();
 }
 
