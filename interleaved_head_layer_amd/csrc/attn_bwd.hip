@@ -622,6 +622,164 @@ __device__ __forceinline__ void bwd_split_body(const AttnBwdArgs& a, SplitSmem<D
   }
 }
 
+// dQ with 32-key tiles copied straight from global memory into LDS (K rows, V rows, K^T: 24 KB
+// per stage at d = 128), so that two workgroups fit per CU; the same products as bwd_dq_kernel.
+constexpr int KT32 = 32;
+template <int DH>
+struct DqSmem {
+  half_t k[2][KT32 * DH];   // K rows, chunk c of row r at c ^ rswz(r)
+  half_t v[2][KT32 * DH];   // V rows, likewise
+  half_t kt[2][DH * KT32];  // K^T: [channel][key], chunk c of row r at c ^ tswz(r)
+};
+
+// (The bodies of the direct-copy kernels are device functions: a kernel whose own lambdas
+// issue the LDS-writing buffer loads loses its host-side launch stub with this compiler.)
+template <int DH, int MASK>
+__device__ __forceinline__ void bwd_dq_direct_body(const AttnBwdArgs& a, DqSmem<DH>& sm) {
+  constexpr int NKS = DH / 16, NCB = DH / 32, CH = DH / 8;
+  constexpr int RR = KT32 * CH / BThreads, TR = DH * 4 / BThreads;
+  static_assert(RR * BThreads == KT32 * CH && TR * BThreads == DH * 4, "tile split");
+  const int L = a.L, H = a.H, window = a.window, Lp = a.Lp;
+  const int nqt = (L + QRows - 1) / QRows;
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = lid / nqt, qt = MASK == kMaskCausal ? nqt - 1 - lid % nqt : lid % nqt;
+  const int b = bh / H, h = bh % H, q0 = qt * QRows;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t rs = static_cast<int64_t>(H) * DH;
+  const int64_t rbase = static_cast<int64_t>(b) * L * rs + h * DH;
+  const int64_t tbase = static_cast<int64_t>(b * H + h) * DH * Lp;
+  const int64_t sbase = static_cast<int64_t>(b * H + h) * L;
+  const int r0 = q0 + 32 * w, qrow = r0 + l32, qload = min(qrow, L - 1);
+
+  const int rbytes = static_cast<int>(((static_cast<int64_t>(L) - 1) * rs + DH) * 2);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(a.K + rbase),
+                                                                        static_cast<short>(0), rbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(a.V + rbase),
+                                                                        static_cast<short>(0), rbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(a.KT + tbase),
+                                                                        static_cast<short>(0), DH * Lp * 2, 0x00020000);
+  unsigned roff[RR], toff[TR];
+#pragma unroll
+  for (int p = 0; p < RR; ++p) {
+    const int P = (p * BWaves + w) * 64 + lane, r = P / CH, c = (P % CH) ^ rswz<DH>(r);
+    roff[p] = static_cast<unsigned>((r * rs + c * 8) * 2);
+  }
+#pragma unroll
+  for (int p = 0; p < TR; ++p) {
+    const int P = (p * BWaves + w) * 64 + lane, r = P / 4, c = (P % 4) ^ tswz(r);
+    toff[p] = static_cast<unsigned>((static_cast<int64_t>(r) * Lp + c * 8) * 2);
+  }
+  auto issue = [&](int k0, int st) {
+    const unsigned rso = static_cast<unsigned>(k0 * rs * 2), tso = static_cast<unsigned>(k0 * 2);
+#pragma unroll
+    for (int p = 0; p < RR; ++p) {
+      const int ld = (p * BWaves + w) * 512;  // halves
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)(sm.k[st] + ld), 16,
+                                               roff[p], rso, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)(sm.v[st] + ld), 16,
+                                               roff[p], rso, 0, 0);
+    }
+#pragma unroll
+    for (int p = 0; p < TR; ++p) {
+      const int ld = (p * BWaves + w) * 512;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(trs, (__attribute__((address_space(3))) void*)(sm.kt[st] + ld), 16,
+                                               toff[p], tso, 0, 0);
+    }
+  };
+
+  int klo = 0, khi = L;
+  if (MASK != kMaskNone) khi = min(L, q0 + QRows);
+  if (MASK == kMaskWindow) klo = max(0, q0 - window + 1);
+  const int kt0 = klo / KT32, kt1 = (khi + KT32 - 1) / KT32;
+  if (kt0 < kt1) issue(kt0 * KT32, 0);
+
+  // This lane's row: Q*scale and dO fragments (B operands), and D = dO . O over the row.
+  half8 qf[NKS], gf[NKS];
+  float dd = 0.f;
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    const int64_t off = rbase + static_cast<int64_t>(qload) * rs + (2 * s + hf) * 8;
+    qf[s] = *reinterpret_cast<const half8*>(a.Qs + off);
+    gf[s] = *reinterpret_cast<const half8*>(a.dO + off);
+    const half8 of = *reinterpret_cast<const half8*>(a.O + off);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dd = fmaf(static_cast<float>(gf[s][e]), static_cast<float>(of[e]), dd);
+  }
+  dd += __shfl_xor(dd, 32);
+  const float lse = qrow < L ? a.lse[sbase + qrow] : __builtin_inff();
+  if (hf == 0 && qrow < L) a.D[sbase + qrow] = dd;
+
+  floatx16 acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
+  wait_vmem();
+  __syncthreads();
+  const int kr = sigma(l32);
+  for (int kti = kt0; kti < kt1; ++kti) {
+    const int k0 = kti * KT32, st = (kti - kt0) & 1;
+    if (kti + 1 < kt1) issue(k0 + KT32, st ^ 1);
+    bool act = true, edge = k0 + KT32 > L || r0 + 32 > L;
+    if (MASK != kMaskNone) {
+      act = k0 <= r0 + 31;
+      edge |= k0 + KT32 - 1 > r0;
+    }
+    if (MASK == kMaskWindow) {
+      act = act && (k0 + KT32 - 1 > r0 - window);
+      edge |= k0 <= r0 + 31 - window;
+    }
+    if (act) {
+      floatx16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+      for (int k = 0; k < NKS; ++k) {
+        const int off = kr * DH + ((2 * k + hf) ^ rswz<DH>(kr)) * 8;
+        s = mfma32(*reinterpret_cast<const half8*>(sm.k[st] + off), qf[k], s);
+        dp = mfma32(*reinterpret_cast<const half8*>(sm.v[st] + off), gf[k], dp);
+      }
+      // Lane (l32, hf), accumulator r: query qrow, key k0 + 16*hf + r.
+      half8 dsf[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float g = fast_exp2(s[r] - lse) * (dp[r] - dd);
+        if (edge && !seen<MASK>(qrow, k0 + 16 * hf + r, L, window)) g = 0.f;
+        dsf[r >> 3][r & 7] = static_cast<half_t>(g);
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const int c = cb * 32 + l32, off = c * KT32 + ((2 * hf + s2) ^ tswz(c)) * 8;
+          acc[cb] = mfma32(*reinterpret_cast<const half8*>(sm.kt[st] + off), dsf[s2], acc[cb]);
+        }
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+  if (qrow < L) {
+    float* dst = a.dQ + rbase + static_cast<int64_t>(qrow) * rs;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        floatx4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[cb][4 * q4 + e] * a.dq_scale;
+        *reinterpret_cast<floatx4*>(dst + cb * 32 + 8 * q4 + 4 * hf) = v;
+      }
+  }
+}
+
+// dQ: about 190 registers at d = 128, two workgroups per CU.
+template <int DH, int MASK>
+__global__ __launch_bounds__(BThreads, 2) void bwd_dq_direct_kernel(AttnBwdArgs a) {
+  __shared__ __attribute__((aligned(16))) DqSmem<DH> sm;
+  bwd_dq_direct_body<DH, MASK>(a, sm);
+}
+
 // dV: about 150-160 registers at d = 128, three workgroups per CU; dK: about 200, two.
 template <int DH, int MASK>
 __global__ __launch_bounds__(BThreads, 3) void bwd_dv_kernel(AttnBwdArgs a) {
@@ -637,12 +795,16 @@ __global__ __launch_bounds__(BThreads, 2) void bwd_dk_kernel(AttnBwdArgs a) {
 template <int DH, int MASK>
 hipError_t launch_grads(const AttnBwdArgs& a, hipStream_t s) {
   const int nqt = (a.L + QRows - 1) / QRows, nkt = (a.L + KRows - 1) / KRows;
-  hipLaunchKernelGGL((bwd_dq_kernel<DH, MASK>), dim3(nqt * a.H * a.B), dim3(BThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   // Direct tile copies need 32-bit byte offsets within one (b, h)'s rows and channel-major copy.
   const bool direct = static_cast<int64_t>(a.L) * a.H * DH * 2 < (int64_t{1} << 31) &&
                       static_cast<int64_t>(DH) * a.Lp * 2 < (int64_t{1} << 31);
+  // dQ first: it writes D = dO . O, which dK reads.
+  if (direct)
+    hipLaunchKernelGGL((bwd_dq_direct_kernel<DH, MASK>), dim3(nqt * a.H * a.B), dim3(BThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<DH, MASK>), dim3(nqt * a.H * a.B), dim3(BThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (direct) {
     hipLaunchKernelGGL((bwd_dv_kernel<DH, MASK>), dim3(nkt * a.H * a.B), dim3(BThreads), 0, s, a);
     e = hipGetLastError();
