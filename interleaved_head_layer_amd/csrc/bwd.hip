@@ -16,92 +16,161 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 // ------------------------------------------------------------------- head reduction
-// out[a][hj] = sum over tokens t and channels c of A[t][a][c] * B[t][hj][c], where B's row
-// for hj = h*P + j is stacked row t*P + j, head h.  A block owns a 16 (a) x 16 (hj) output
-// tile and a chunk of tokens; each thread one output.  TS tokens at a time pass through LDS
-// (rows padded by 4 floats so the 16 hj rows a wave reads fall in different banks).
-constexpr int kRedTile = 16;
-constexpr int kRedChunkTarget = 2048;  // chunks x tiles is about this (bounds the partials)
+// out[a][hj] = sum over tokens t and channels c of A[t][a][c] * B[t][hj][c], where B's row for
+// hj = h*P + j is stacked row t*P + j, head h: a product whose contracted dimension is (t, c).
+// It runs on the matrix cores straight from global memory: a workgroup of 4 waves owns a chunk
+// of tokens and a group of up to kRedCB 32-wide hj blocks (grid.y); each wave takes every 4th
+// token and accumulates the whole (a, hj) tile.  Per 16-channel step a lane loads 8 channels of
+// its A row (a = lane % 32 + 32 rb) and of its B row (hj = lane % 32 + 32 cb), splits them into
+// bf16 high and low parts and issues hi*hi + hi*lo + lo*hi (about 2^-16 relative per product,
+// fp32 accumulation).  Every operand element is read once.  The waves' tiles are added in LDS
+// in wave order and written as the chunk's partial sums.
+constexpr int kRedCB = 3;               // hj blocks per workgroup
+constexpr int kRedChunkTarget = 512;    // chunks x hj groups is about this (bounds the partials)
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ void split_bf16(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint16_t h = f32_to_bf16(x[e]);
+    const uint16_t l = f32_to_bf16(x[e] - __uint_as_float(static_cast<uint32_t>(h) << 16));
+    hi[e] = __builtin_bit_cast(__bf16, h);
+    lo[e] = __builtin_bit_cast(__bf16, l);
+  }
+}
 
 template <typename TB>
-__device__ __forceinline__ floatx4 load4(const TB* p);
+__device__ __forceinline__ void load8(const TB* p, float (&x)[8]);
 template <>
-__device__ __forceinline__ floatx4 load4<float>(const float* p) {
-  return *reinterpret_cast<const floatx4*>(p);
+__device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
+  const floatx4 u = *reinterpret_cast<const floatx4*>(p), v = *reinterpret_cast<const floatx4*>(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = u[e];
+    x[4 + e] = v[e];
+  }
 }
 template <>
-__device__ __forceinline__ floatx4 load4<half_t>(const half_t* p) {
-  typedef half_t half4 __attribute__((ext_vector_type(4)));
-  const half4 h = *reinterpret_cast<const half4*>(p);
-  return floatx4{static_cast<float>(h[0]), static_cast<float>(h[1]), static_cast<float>(h[2]),
-                 static_cast<float>(h[3])};
+__device__ __forceinline__ void load8<half_t>(const half_t* p, float (&x)[8]) {
+  const half8 u = *reinterpret_cast<const half8*>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = static_cast<float>(u[e]);
 }
 
-template <typename TB, int DH>
+template <typename TB, int DH, int RB>
 __global__ __launch_bounds__(256) void head_reduce_kernel(const float* __restrict__ A, int64_t lda,
                                                           const TB* __restrict__ Bm, float* __restrict__ part,
                                                           int ntok, int H, int P, int tpc) {
-  constexpr int TS = 256 / DH;  // tokens per LDS stage
-  constexpr int LD = DH + 4;
-  __shared__ float as[TS][kRedTile][LD];
-  __shared__ float bs[TS][kRedTile][LD];
+  constexpr int NS = DH / 16;
+  __shared__ float red[RB * 32][kRedCB * 32 + 1];
   const int HP = H * P;
-  const int a0 = blockIdx.y * kRedTile, hj0 = blockIdx.z * kRedTile;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int cb0 = blockIdx.y * kRedCB;
   const int t_begin = blockIdx.x * tpc, t_end = min(ntok, t_begin + tpc);
-  const int tid = threadIdx.x, ty = tid / kRedTile, tx = tid % kRedTile;
-  float acc = 0.f;
-  for (int t0 = t_begin; t0 < t_end; t0 += TS) {
-    // TS x 16 rows x DH channels of each operand = 1024 float4 = 4 per thread
+  floatx16 acc[RB][kRedCB];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = tid + 256 * q, row = e / (DH / 4), c = (e % (DH / 4)) * 4;
-      const int ts = row / kRedTile, r = row % kRedTile, t = t0 + ts;
-      floatx4 va{0.f, 0.f, 0.f, 0.f}, vb{0.f, 0.f, 0.f, 0.f};
-      if (t < t_end && a0 + r < H) va = load4<float>(A + static_cast<int64_t>(t) * lda + (a0 + r) * DH + c);
-      const int hj = hj0 + r;
-      if (t < t_end && hj < HP) {
-        const int h = hj / P, j = hj % P;
-        vb = load4<TB>(Bm + ((static_cast<int64_t>(t) * P + j) * H + h) * DH + c);
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < kRedCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
+  // This lane's A rows and B rows (invalid ones read row 0 and are multiplied by zero: their
+  // products land in rows / columns that are never written out).
+  int arow[RB];
+  bool aval[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    aval[rb] = rb * 32 + l32 < H;
+    arow[rb] = aval[rb] ? rb * 32 + l32 : 0;
+  }
+  int64_t boff[kRedCB];
+  bool bval[kRedCB];
+#pragma unroll
+  for (int cb = 0; cb < kRedCB; ++cb) {
+    const int hj = (cb0 + cb) * 32 + l32;
+    bval[cb] = hj < HP;
+    const int hh = bval[cb] ? hj / P : 0, j = bval[cb] ? hj % P : 0;
+    boff[cb] = (static_cast<int64_t>(j) * H + hh) * DH;  // + t*P*H*DH
+  }
+  for (int t = t_begin + w; t < t_end; t += 4) {
+    const float* at = A + static_cast<int64_t>(t) * lda;
+    const TB* bt = Bm + static_cast<int64_t>(t) * P * H * DH;
+#pragma unroll 2
+    for (int s = 0; s < NS; ++s) {
+      const int c = s * 16 + 8 * hf;
+      bf16x8 ah[RB], al[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float x[8];
+        load8<float>(at + arow[rb] * DH + c, x);
+        if (!aval[rb])
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        split_bf16(x, ah[rb], al[rb]);
       }
-      *reinterpret_cast<floatx4*>(&as[ts][r][c]) = va;
-      *reinterpret_cast<floatx4*>(&bs[ts][r][c]) = vb;
+#pragma unroll
+      for (int cb = 0; cb < kRedCB; ++cb) {
+        float x[8];
+        load8<TB>(bt + boff[cb] + c, x);
+        if (!bval[cb])
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        bf16x8 bh, bl;
+        split_bf16(x, bh, bl);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[rb], bh, acc[rb][cb], 0, 0, 0);
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[rb], bl, acc[rb][cb], 0, 0, 0);
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[rb], bh, acc[rb][cb], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // Lane l holds C[8*(r/4) + 4*hf + r%4][l%32] of each 32x32 block: add the waves in order.
+  for (int ww = 0; ww < 4; ++ww) {
+    if (w == ww) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < kRedCB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float& dst = red[rb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3)][cb * 32 + l32];
+            dst = ww == 0 ? acc[rb][cb][r] : dst + acc[rb][cb][r];
+          }
     }
     __syncthreads();
-#pragma unroll
-    for (int ts = 0; ts < TS; ++ts)
-#pragma unroll 8
-      for (int c = 0; c < DH; c += 4) {
-        const floatx4 x = *reinterpret_cast<const floatx4*>(&as[ts][ty][c]);
-        const floatx4 y = *reinterpret_cast<const floatx4*>(&bs[ts][tx][c]);
-        acc += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
-      }
-    __syncthreads();
   }
-  const int a = a0 + ty, hj = hj0 + tx;
-  if (a < H && hj < HP) part[static_cast<int64_t>(blockIdx.x) * H * HP + a * HP + hj] = acc;
+  for (int e = tid; e < RB * 32 * kRedCB * 32; e += 256) {
+    const int a = e / (kRedCB * 32), hj = cb0 * 32 + e % (kRedCB * 32);
+    if (a < H && hj < HP) part[static_cast<int64_t>(blockIdx.x) * H * HP + a * HP + hj] = red[a][hj - cb0 * 32];
+  }
 }
 
-// out[o] = sum over chunks of part[chunk][o], chunks in order.
+// out[o] = sum over chunks of part[chunk][o]: one wave per output, lane k adding chunks k, k+64,
+// ... in order, then a fixed shuffle tree (the same order on every call).
 __global__ __launch_bounds__(256) void head_reduce_sum_kernel(const float* __restrict__ part, float* __restrict__ out,
                                                               int n, int nchunks) {
-  const int o = blockIdx.x * 256 + threadIdx.x;
+  const int o = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (o >= n) return;
   float s = 0.f;
-  for (int k = 0; k < nchunks; ++k) s += part[static_cast<int64_t>(k) * n + o];
-  out[o] = s;
+  for (int k = lane; k < nchunks; k += 64) s += part[static_cast<int64_t>(k) * n + o];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  if (lane == 0) out[o] = s;
 }
 
 struct RedPlan {
-  int tiles_y, tiles_z, nchunks, tpc;
+  int groups, nchunks, tpc;
 };
 
 RedPlan red_plan(int ntok, int H, int P) {
   RedPlan p{};
-  p.tiles_y = (H + kRedTile - 1) / kRedTile;
-  p.tiles_z = (H * P + kRedTile - 1) / kRedTile;
-  const int target = std::max(1, kRedChunkTarget / (p.tiles_y * p.tiles_z));
+  const int cbs = (H * P + 31) / 32;
+  p.groups = (cbs + kRedCB - 1) / kRedCB;
+  const int target = std::max(1, kRedChunkTarget / p.groups);
   const int ntok1 = std::max(ntok, 1);
-  p.tpc = std::max(1, (ntok1 + target - 1) / target);
+  p.tpc = std::max(4, (ntok1 + target - 1) / target);
   p.nchunks = (ntok1 + p.tpc - 1) / p.tpc;
   return p;
 }
@@ -184,28 +253,26 @@ size_t head_reduce_part_bytes(int ntok, int H, int P) {
 
 hipError_t launch_head_reduce(const float* A, int64_t lda, const void* Bm, bool b_half, float* out, float* part,
                               int ntok, int H, int P, int d, hipStream_t s) {
-  if (d != 64 && d != 128) return hipErrorInvalidValue;
+  if ((d != 64 && d != 128) || H > 64) return hipErrorInvalidValue;
   const RedPlan p = red_plan(ntok, H, P);
-  const dim3 grid(p.nchunks, p.tiles_y, p.tiles_z);
+  const dim3 grid(p.nchunks, p.groups);
+  auto go = [&](auto kern, const auto* b) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, A, lda, b, part, ntok, H, P, p.tpc);
+  };
+  const half_t* bh = static_cast<const half_t*>(Bm);
+  const float* bf = static_cast<const float*>(Bm);
+  const bool two = H > 32;
   if (d == 64) {
-    if (b_half)
-      hipLaunchKernelGGL((head_reduce_kernel<half_t, 64>), grid, dim3(256), 0, s, A, lda,
-                         static_cast<const half_t*>(Bm), part, ntok, H, P, p.tpc);
-    else
-      hipLaunchKernelGGL((head_reduce_kernel<float, 64>), grid, dim3(256), 0, s, A, lda,
-                         static_cast<const float*>(Bm), part, ntok, H, P, p.tpc);
+    if (b_half) two ? go(head_reduce_kernel<half_t, 64, 2>, bh) : go(head_reduce_kernel<half_t, 64, 1>, bh);
+    else two ? go(head_reduce_kernel<float, 64, 2>, bf) : go(head_reduce_kernel<float, 64, 1>, bf);
   } else {
-    if (b_half)
-      hipLaunchKernelGGL((head_reduce_kernel<half_t, 128>), grid, dim3(256), 0, s, A, lda,
-                         static_cast<const half_t*>(Bm), part, ntok, H, P, p.tpc);
-    else
-      hipLaunchKernelGGL((head_reduce_kernel<float, 128>), grid, dim3(256), 0, s, A, lda,
-                         static_cast<const float*>(Bm), part, ntok, H, P, p.tpc);
+    if (b_half) two ? go(head_reduce_kernel<half_t, 128, 2>, bh) : go(head_reduce_kernel<half_t, 128, 1>, bh);
+    else two ? go(head_reduce_kernel<float, 128, 2>, bf) : go(head_reduce_kernel<float, 128, 1>, bf);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n = H * H * P;
-  hipLaunchKernelGGL(head_reduce_sum_kernel, dim3((n + 255) / 256), dim3(256), 0, s, part, out, n, p.nchunks);
+  hipLaunchKernelGGL(head_reduce_sum_kernel, dim3((n + 3) / 4), dim3(256), 0, s, part, out, n, p.nchunks);
   return hipGetLastError();
 }
 

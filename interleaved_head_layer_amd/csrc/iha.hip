@@ -769,16 +769,18 @@ iha_status iha_backward(const iha_problem* prob, const void* X, const void* W_Q,
   // tokens, dX = sum_m (dY_m high + low) W_m^T as one product over 6D.
   for (int half = 0; half < 2; ++half)
     IHA_HIP(iha::launch_to_bf16_t(X, true, D, M, D, Xt + half * Mp, nullptr, 2 * Mp, Mp, stream));
-  for (int w = 0; w < 3; ++w) {
-    iha::NtArgs g{};
+  {
+    iha::NtArgs g{};  // the three weight gradients in one launch (about 3x the workgroups of one)
     g.A = Xt;
-    g.B = dYt + static_cast<int64_t>(w) * D * 2 * Mp;
-    g.C = dWs[w];
+    g.sa = 0;
+    g.B = dYt;
+    g.sb = static_cast<int64_t>(D) * 2 * Mp;
+    for (int w = 0; w < 3; ++w) g.Cz[w] = dWs[w];
     g.I = D;
     g.J = D;
     g.K = static_cast<int>(2 * Mp);
     g.ldc = D;
-    IHA_HIP(iha::launch_gemm_nt_bf16(g, stream));
+    IHA_HIP(iha::launch_gemm_nt_batched(g, 3, stream));
   }
   iha::NtArgs g{};
   g.A = dYcat;

@@ -125,6 +125,9 @@ struct NtArgs {
   int I, J, K;
   int64_t ldc;
   int jbase;          // fused mixing: global token of B's row 0 (the launcher splits tokens)
+  // launch_gemm_nt_batched: product z (blockIdx.y) reads A + z*sa, B + z*sb, writes Cz[z].
+  int64_t sa, sb;
+  float* Cz[3];
 };
 struct ProjArgs {
   const uint16_t* X;      // [B*N][D] bf16
@@ -167,6 +170,10 @@ hipError_t launch_proj_bf16(const ProjArgs& pa, hipStream_t s, hipEvent_t ev_pre
 hipError_t launch_proj_rowmajor(ProjArgs pa, hipStream_t s);
 // C[I][ldc] = A[I][K] B[J][K]^T, bf16 operands (K a multiple of 64), fp32 result.
 hipError_t launch_gemm_nt_bf16(const NtArgs& g, hipStream_t s);
+// `batch` (<= 3) such products of one shape in one launch: product z takes A + z*sa and
+// B + z*sb and writes Cz[z] (g.C unused); one product after another where the shape needs the
+// launcher's 2 GiB split.
+hipError_t launch_gemm_nt_batched(const NtArgs& g, int batch, hipStream_t s);
 // The gradient of the collapse with respect to the stacked outputs:
 //   out[b][t*P + j][h'][c] = sum_h R[h][h'*P + j] * G[b][t][h*d + c]
 // G fp32 [B*N][H*d] (16-byte aligned), out fp16 [B][N*P][H][d].

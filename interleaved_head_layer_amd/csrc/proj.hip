@@ -197,6 +197,12 @@ __device__ __forceinline__ void gemm_tile(const NtArgs& g, NtSmem<RBW>& sm, Epi&
 
 __global__ __launch_bounds__(GThreads, 1) void gemm_nt_bf16_kernel(NtArgs g) {
   __shared__ __attribute__((aligned(16))) NtSmem<GRBW> sm;
+  if (gridDim.y > 1) {  // batched launch: product blockIdx.y
+    const int z = blockIdx.y;
+    g.A += z * g.sa;
+    g.B += z * g.sb;
+    g.C = g.Cz[z];
+  }
   gemm_tile<GRBW>(g, sm, [&](floatx16 (&acc)[GRBW][2], int i0, int j0, int wm, int wn) {
     const int lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5;
     const int I = g.I, J = g.J;
@@ -789,6 +795,25 @@ void launch_mix_rows(const ProjArgs& pa, int nmat, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_nt_bf16(const NtArgs& g, hipStream_t s) { return launch_gemm_nt(g, s); }
+
+hipError_t launch_gemm_nt_batched(const NtArgs& g, int batch, hipStream_t s) {
+  if (batch < 1 || batch > 3) return hipErrorInvalidValue;
+  const int64_t max_rows = ((int64_t{1} << 31) - 1) / (static_cast<int64_t>(g.K) * 2) / GTI * GTI;
+  if (batch == 1 || max_rows < g.I || max_rows < g.J) {
+    for (int z = 0; z < batch; ++z) {
+      NtArgs c = g;
+      c.A = g.A + z * g.sa;
+      c.B = g.B + z * g.sb;
+      c.C = g.Cz[z];
+      const hipError_t e = launch_gemm_nt(c, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  const int tiles = ((g.I + GTI - 1) / GTI) * ((g.J + GTJ - 1) / GTJ);
+  hipLaunchKernelGGL(gemm_nt_bf16_kernel, dim3(tiles, batch), dim3(GThreads), 0, s, g);
+  return hipGetLastError();
+}
 
 hipError_t launch_expand(const float* G, const float* Rm, half_t* out, int B, int N, int H, int P, int d,
                          hipStream_t s) {
