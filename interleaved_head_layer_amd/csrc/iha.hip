@@ -372,10 +372,20 @@ iha_status bwd_validate(int64_t B, int64_t L, int64_t H, int64_t d, int32_t mask
 // Workspace of iha_backward (bf16 inputs).  The fp32 projections Y = X [W_Q | W_K | W_V] are
 // kept for the mixing gradient and then overwritten with the projection gradients dY.
 struct LayerBwdLayout {
-  size_t flag, wt, y, qb, kb, vb, dpb, dq, dk, dv, att, part, dycat, dyt, xt, wcat, total;
+  size_t flag, wt, y, qb, kb, vb, dpb, dq, dk, dv, att, part, dycat, dyt, xt, wcat, wsplit, total;
   int64_t Mp;  // tokens rounded up to 64 (the K dimension of the weight-gradient GEMM)
+  int splits;  // parts of the weight-gradient GEMM's contracted (token) dimension
   BwdLayout a;
 };
+
+// The three weight-gradient products have few 256 x 256 tiles (D/256 squared each): split their
+// 2 Mp-long contracted dimension until the launch has about three rounds of workgroups.
+int dw_splits(int64_t D, int64_t Mp) {
+  const int64_t tiles = ((D + 255) / 256) * ((D + 255) / 256);
+  int s = 1;
+  while (s < 4 && 3 * tiles * s < 3 * 256 && (2 * Mp) % (64 * 2 * s) == 0) s *= 2;
+  return s;
+}
 
 LayerBwdLayout layer_bwd_layout(const iha_problem& p) {
   LayerBwdLayout l{};
@@ -407,6 +417,8 @@ LayerBwdLayout layer_bwd_layout(const iha_problem& p) {
   l.dyt = take(3 * D * 2 * static_cast<size_t>(l.Mp) * 2);
   l.xt = take(D * 2 * static_cast<size_t>(l.Mp) * 2);
   l.wcat = take(D * 6 * D * 2);
+  l.splits = dw_splits(static_cast<int64_t>(D), l.Mp);
+  l.wsplit = take(l.splits > 1 ? static_cast<size_t>(l.splits) * 3 * D * D * 4 : 0);
   l.total = off;
   return l;
 }
@@ -770,7 +782,7 @@ iha_status iha_backward(const iha_problem* prob, const void* X, const void* W_Q,
   for (int half = 0; half < 2; ++half)
     IHA_HIP(iha::launch_to_bf16_t(X, true, D, M, D, Xt + half * Mp, nullptr, 2 * Mp, Mp, stream));
   {
-    iha::NtArgs g{};  // the three weight gradients in one launch (about 3x the workgroups of one)
+    iha::NtArgs g{};  // the three weight gradients in one launch, the token dimension split
     g.A = Xt;
     g.sa = 0;
     g.B = dYt;
@@ -780,7 +792,7 @@ iha_status iha_backward(const iha_problem* prob, const void* X, const void* W_Q,
     g.J = D;
     g.K = static_cast<int>(2 * Mp);
     g.ldc = D;
-    IHA_HIP(iha::launch_gemm_nt_batched(g, 3, stream));
+    IHA_HIP(iha::launch_gemm_nt_splitk(g, 3, lay.splits, reinterpret_cast<float*>(ws + lay.wsplit), stream));
   }
   iha::NtArgs g{};
   g.A = dYcat;

@@ -128,6 +128,7 @@ struct NtArgs {
   // launch_gemm_nt_batched: product z (blockIdx.y) reads A + z*sa, B + z*sb, writes Cz[z].
   int64_t sa, sb;
   float* Cz[3];
+  int ks;  // row stride of A and B in elements (0: K); a split-K launch reads K-wide column slices
 };
 struct ProjArgs {
   const uint16_t* X;      // [B*N][D] bf16
@@ -174,6 +175,10 @@ hipError_t launch_gemm_nt_bf16(const NtArgs& g, hipStream_t s);
 // B + z*sb and writes Cz[z] (g.C unused); one product after another where the shape needs the
 // launcher's 2 GiB split.
 hipError_t launch_gemm_nt_batched(const NtArgs& g, int batch, hipStream_t s);
+// The same `batch` products with the contracted dimension g.K split into `splits` equal parts
+// (g.K / splits a multiple of 64): part p of product z goes to Cs + (p*batch + z)*I*ldc, then a
+// second kernel adds the parts in order into Cz[z].  Cs holds splits*batch*I*ldc floats.
+hipError_t launch_gemm_nt_splitk(const NtArgs& g, int batch, int splits, float* Cs, hipStream_t s);
 // The gradient of the collapse with respect to the stacked outputs:
 //   out[b][t*P + j][h'][c] = sum_h R[h][h'*P + j] * G[b][t][h*d + c]
 // G fp32 [B*N][H*d] (16-byte aligned), out fp16 [B][N*P][H][d].

@@ -86,6 +86,7 @@ template <int RBW, typename Epi>
 __device__ __forceinline__ void gemm_tile(const NtArgs& g, NtSmem<RBW>& sm, Epi&& epi) {
   constexpr int TI = 64 * RBW;
   const int I = g.I, J = g.J, K = g.K;
+  const int64_t KS = g.ks > 0 ? g.ks : K;  // row stride of A and B
   const int ntj = (J + GTJ - 1) / GTJ, nti = (I + TI - 1) / TI;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   // Groups of 4 row tiles sweep the column tiles, so a group's A slices stay in L2.
@@ -101,25 +102,26 @@ __device__ __forceinline__ void gemm_tile(const NtArgs& g, NtSmem<RBW>& sm, Epi&
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
 
+  // Readable bytes end with the last valid row's K values: rows past I / J read zero.
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(g.A), static_cast<short>(0), static_cast<int>(static_cast<int64_t>(I) * K * 2), 0x00020000);
+      const_cast<uint16_t*>(g.A), static_cast<short>(0), static_cast<int>(((I - 1) * KS + K) * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(g.B), static_cast<short>(0), static_cast<int>(static_cast<int64_t>(J) * K * 2), 0x00020000);
+      const_cast<uint16_t*>(g.B), static_cast<short>(0), static_cast<int>(((J - 1) * KS + K) * 2), 0x00020000);
   // Copy slot (p * 8 + wave) * 64 + lane of a stage -> row 64p + 8 * wave + lane / 8, chunk
   // lane % 8; the swizzle depends on the row only through 8 * wave + lane / 8.
   const int rl = 8 * wave + (lane >> 3), pos = lane & 7;
-  const unsigned loff = static_cast<unsigned>((rl * K + (pos ^ gswz(rl)) * 8) * 2);
+  const unsigned loff = static_cast<unsigned>((rl * KS + (pos ^ gswz(rl)) * 8) * 2);
   auto issue = [&](int k0, int st) {
 #pragma unroll
     for (int p = 0; p < TI / 64; ++p)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ra, (__attribute__((address_space(3))) void*)(sm.a[st] + (p * GWaves + wave) * 512), 16, loff,
-          static_cast<unsigned>((static_cast<int64_t>(i0 + 64 * p) * K + k0) * 2), 0, 0);
+          static_cast<unsigned>((static_cast<int64_t>(i0 + 64 * p) * KS + k0) * 2), 0, 0);
 #pragma unroll
     for (int p = 0; p < GTJ / 64; ++p)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rb, (__attribute__((address_space(3))) void*)(sm.b[st] + (p * GWaves + wave) * 512), 16, loff,
-          static_cast<unsigned>((static_cast<int64_t>(j0 + 64 * p) * K + k0) * 2), 0, 0);
+          static_cast<unsigned>((static_cast<int64_t>(j0 + 64 * p) * KS + k0) * 2), 0, 0);
   };
 
   // Per-lane LDS element offsets of the A / B fragments; k-step s reads chunk 2s + hf.
@@ -197,11 +199,11 @@ __device__ __forceinline__ void gemm_tile(const NtArgs& g, NtSmem<RBW>& sm, Epi&
 
 __global__ __launch_bounds__(GThreads, 1) void gemm_nt_bf16_kernel(NtArgs g) {
   __shared__ __attribute__((aligned(16))) NtSmem<GRBW> sm;
-  if (gridDim.y > 1) {  // batched launch: product blockIdx.y
-    const int z = blockIdx.y;
-    g.A += z * g.sa;
-    g.B += z * g.sb;
-    g.C = g.Cz[z];
+  if (gridDim.y > 1 || gridDim.z > 1) {  // batched launch: product blockIdx.y, K part blockIdx.z
+    const int z = blockIdx.y, sp = blockIdx.z;
+    g.A += z * g.sa + static_cast<int64_t>(sp) * g.K;
+    g.B += z * g.sb + static_cast<int64_t>(sp) * g.K;
+    g.C = gridDim.z > 1 ? g.C + (static_cast<int64_t>(sp) * gridDim.y + z) * g.I * g.ldc : g.Cz[z];
   }
   gemm_tile<GRBW>(g, sm, [&](floatx16 (&acc)[GRBW][2], int i0, int j0, int wm, int wn) {
     const int lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5;
@@ -795,6 +797,39 @@ void launch_mix_rows(const ProjArgs& pa, int nmat, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_nt_bf16(const NtArgs& g, hipStream_t s) { return launch_gemm_nt(g, s); }
+
+// Cz[z][e] = sum over parts p (in order) of Cs[(p*batch + z)*n + e], n = I * ldc.
+__global__ __launch_bounds__(256) void splitk_sum_kernel(NtArgs g, int batch, int splits, int64_t n) {
+  const int z = blockIdx.y;
+  const floatx4* src = reinterpret_cast<const floatx4*>(g.C);
+  floatx4* dst = reinterpret_cast<floatx4*>(g.Cz[z]);
+  const int64_t n4 = n / 4;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n4; e += static_cast<int64_t>(gridDim.x) * 256) {
+    floatx4 acc = src[static_cast<int64_t>(z) * n4 + e];
+    for (int p = 1; p < splits; ++p) acc += src[(static_cast<int64_t>(p) * batch + z) * n4 + e];
+    dst[e] = acc;
+  }
+}
+
+hipError_t launch_gemm_nt_splitk(const NtArgs& g, int batch, int splits, float* Cs, hipStream_t s) {
+  if (batch < 1 || batch > 3 || splits < 1 || g.K % (64 * splits) != 0 || (g.I * g.ldc) % 4 != 0)
+    return hipErrorInvalidValue;
+  if (splits == 1) return launch_gemm_nt_batched(g, batch, s);
+  NtArgs c = g;
+  c.ks = g.ks > 0 ? g.ks : g.K;
+  c.K = g.K / splits;
+  c.C = Cs;
+  const int64_t max_rows = ((int64_t{1} << 31) - 1) / (static_cast<int64_t>(c.ks) * 2) / GTI * GTI;
+  if (max_rows < g.I || max_rows < g.J) return hipErrorInvalidValue;
+  const int tiles = ((g.I + GTI - 1) / GTI) * ((g.J + GTJ - 1) / GTJ);
+  hipLaunchKernelGGL(gemm_nt_bf16_kernel, dim3(tiles, batch, splits), dim3(GThreads), 0, s, c);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = static_cast<int64_t>(g.I) * g.ldc;
+  const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((n / 4 + 255) / 256, 1024));
+  hipLaunchKernelGGL(splitk_sum_kernel, dim3(blocks, batch), dim3(256), 0, s, c, batch, splits, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_nt_batched(const NtArgs& g, int batch, hipStream_t s) {
   if (batch < 1 || batch > 3) return hipErrorInvalidValue;
