@@ -203,7 +203,9 @@ __global__ __launch_bounds__(GThreads, 1) void gemm_nt_bf16_kernel(NtArgs g) {
     const int z = blockIdx.y, sp = blockIdx.z;
     g.A += z * g.sa + static_cast<int64_t>(sp) * g.K;
     g.B += z * g.sb + static_cast<int64_t>(sp) * g.K;
-    g.C = gridDim.z > 1 ? g.C + (static_cast<int64_t>(sp) * gridDim.y + z) * g.I * g.ldc : g.Cz[z];
+    // (Cz by selects: a dynamic index would put the argument block in scratch memory.)
+    g.C = gridDim.z > 1 ? g.C + (static_cast<int64_t>(sp) * gridDim.y + z) * g.I * g.ldc
+                        : z == 0 ? g.Cz[0] : z == 1 ? g.Cz[1] : g.Cz[2];
   }
   gemm_tile<GRBW>(g, sm, [&](floatx16 (&acc)[GRBW][2], int i0, int j0, int wm, int wn) {
     const int lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5;
