@@ -530,7 +530,39 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
   const float lt = st.l + __shfl_xor(st.l, 32);
   if (a.lse && hf == 0 && qrow < L)
     a.lse[static_cast<int64_t>(b * H + h) * L + qrow] = lt > 0.f ? st.m + __log2f(lt) : __builtin_inff();
-  if (qrow < L) {
+  if (a.Oh && !a.Xf && r0 >= a.R2) {
+    // fp16 outputs of a wave whose rows are all past the fp32 ones: the 32 x d block goes
+    // through the wave's own stretch of the idle K/V stages (every copy has landed and every
+    // wave has passed the last barrier), so that each store writes 16 contiguous bytes per
+    // lane and whole rows per instruction instead of 8-byte pieces of 32 rows.
+    constexpr int OLD = DH + 8;  // padded LDS row (halves): rows 68 banks apart
+    static_assert(AWaves * 32 * OLD * 2 <= sizeof(AttnSmem<DH>), "LDS");
+    half_t* ob = reinterpret_cast<half_t*>(&sm) + w * 32 * OLD;
+    float inv = lt;
+    if (lt > 0.f) {
+      inv = 1.f / lt;
+    } else if (lt == 0.f) {
+      inv = 0.f;
+      if (a.flag && qrow < L) atomicOr(a.flag, kFlagEmptyRow);
+    }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        half4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = static_cast<half_t>(st.o[cb][4 * q + e] * inv);
+        *reinterpret_cast<half4*>(ob + l32 * OLD + cb * 32 + 8 * q + 4 * hf) = v;
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // LDS in order within the wave
+    constexpr int CPR = DH / 8;                          // 16-byte chunks per row
+#pragma unroll
+    for (int i = 0; i < 32 * CPR / 64; ++i) {
+      const int idx = i * 64 + lane, row = idx / CPR, ch = idx % CPR;
+      const half8 v = *reinterpret_cast<const half8*>(ob + row * OLD + ch * 8);
+      if (r0 + row < L) *reinterpret_cast<half8*>(a.Oh + obase + static_cast<int64_t>(r0 + row) * rs + ch * 8) = v;
+    }
+  } else if (qrow < L) {
     // lt > 0 for every valid row; lt == 0 means nothing was visible (reported, output 0);
     // a NaN sum (non-finite input) is passed through to the output.
     float inv = lt;
