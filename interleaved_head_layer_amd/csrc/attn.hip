@@ -189,6 +189,7 @@ __device__ __forceinline__ void attn_tile(bool edge, const half_t* __restrict__ 
   half8 kr[NK];
 #pragma unroll
   for (int i = 0; i < kPre; ++i) kr[i] = kfrag(i);
+  __builtin_amdgcn_sched_barrier(0); __builtin_amdgcn_s_setprio(1); __builtin_amdgcn_sched_barrier(0);
   floatx16 s[2];
 #pragma unroll
   for (int i = 0; i < NK; ++i) {
@@ -206,12 +207,20 @@ __device__ __forceinline__ void attn_tile(bool edge, const half_t* __restrict__ 
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+  __builtin_amdgcn_sched_barrier(0); __builtin_amdgcn_s_setprio(0); __builtin_amdgcn_sched_barrier(0);
   if (__builtin_expect(edge, false)) {
+    // Key k0 + 32 kb + 16 hf + r is visible for r in [lo, lo + n): the same rule as visible(),
+    // as one unsigned range test per element.
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      const int base = k0 + kb * 32 + 16 * hf;
+      const int last = (MASK == kMaskNone ? L - 1 : min(qrow, L - 1)) - base;
+      const int lo = max(MASK == kMaskWindow ? qrow - window + 1 - base : 0, 0);
+      const unsigned n = static_cast<unsigned>(max(min(last, 15) + 1 - lo, 0));
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (!visible<MASK>(qrow, k0 + kb * 32 + 16 * hf + r, L, window)) s[kb][r] = -__builtin_inff();
+        if (static_cast<unsigned>(r - lo) >= n) s[kb][r] = -__builtin_inff();
+    }
   }
   half8 pf[2][2];
   // Row sums in fp32 from the unrounded probabilities: plain adds overlap the matrix-core
@@ -273,6 +282,7 @@ __device__ __forceinline__ void attn_tile(bool edge, const half_t* __restrict__ 
     tsum = probs();
   }
   st.l += tsum;
+  __builtin_amdgcn_sched_barrier(0); __builtin_amdgcn_s_setprio(1); __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     if (j + kPre < NV) vr[j + kPre] = vfrag(j + kPre);
@@ -284,6 +294,9 @@ __device__ __forceinline__ void attn_tile(bool edge, const half_t* __restrict__ 
     if (j + kPre < NV) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // ------------------------------------------------------------ fp32 first rows
