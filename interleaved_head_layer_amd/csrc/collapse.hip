@@ -181,7 +181,7 @@ __global__ __launch_bounds__(256) void collapse_h_kernel(CollapseSrc src, const 
 // value (low part zero for its fp16 rows), and takes a third product Rt_hi * low; these
 // tokens come first, one at a time per workgroup.
 template <int KS, int NW>
-__global__ __launch_bounds__(NW * 64) void collapse_mfma_kernel(CollapseSrc src, const float* __restrict__ R,
+__global__ __launch_bounds__(NW * 64, 2) void collapse_mfma_kernel(CollapseSrc src, const float* __restrict__ R,
                                                                float* __restrict__ out, int ntok, int H, int P,
                                                                int d) {
   constexpr int NT = NW * 64;
