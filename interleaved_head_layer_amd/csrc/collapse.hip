@@ -356,8 +356,9 @@ hipError_t launch_collapse_h(const half_t* Ph, const float* Pe, int Rrows, const
   }
   const CollapseSrc src{nullptr, Ph, Pe, Rrows, N, (Rrows + P - 1) / P};
   const int ntok = B * N;
-  // About 8 tokens per workgroup.
-  const int grid = std::max(1, std::min(ntok / 8, 256 * 8));
+  // About 8 tokens per workgroup, but at least 1024 workgroups (or one per token) so that a
+  // short batch still spreads over every compute unit.
+  const int grid = std::max(1, std::min(std::min(ntok, std::max(ntok / 8, 1024)), 256 * 8));
   const size_t lds = 2 * static_cast<size_t>(KS) * 16 * (d + 4) * sizeof(uint16_t);
   auto go = [&](auto kern, int threads) {
     hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), lds, s, src, R, out, ntok, H, P, d);
