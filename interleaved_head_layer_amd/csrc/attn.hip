@@ -548,7 +548,7 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
     // through the wave's own stretch of the idle K/V stages (every copy has landed and every
     // wave has passed the last barrier), so that each store writes 16 contiguous bytes per
     // lane and whole rows per instruction instead of 8-byte pieces of 32 rows.
-    constexpr int OLD = DH + 8;  // padded LDS row (halves): rows 68 banks apart
+    constexpr int OLD = DH + 8;  // padded LDS row (halves): the 32 rows' writes spread over the banks
     static_assert(AWaves * 32 * OLD * 2 <= sizeof(AttnSmem<DH>), "LDS");
     half_t* ob = reinterpret_cast<half_t*>(&sm) + w * 32 * OLD;
     float inv = lt;
