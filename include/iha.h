@@ -224,7 +224,7 @@ iha_status iha_attention(int64_t B, int64_t L, int64_t H, int64_t d, int32_t mas
  * Operands of the matrix-core products are fp16 (the probabilities and dS
  * rounded to fp16), accumulation fp32.  dS = A * (dO_i . V_k - D_i) is finite in fp16
  * while |dO_i . V_k - D_i| stays below 65504 (for example every element of dO and V
- * below 20 in magnitude at d = 128); beyond that the gradients of the affected rows
+ * below 14 in magnitude at d = 128, as |D_i| <= max_k |dO_i . V_k|); beyond that the gradients of the affected rows
  * become infinite, and this entry point has no checking flag (iha_backward's
  * IHA_FLAG_CHECK reports non-finite gradients).  Enqueued on `stream`, no wait. */
 iha_status iha_attention_backward_workspace(int64_t B, int64_t L, int64_t H, int64_t d,
