@@ -235,8 +235,9 @@ __device__ __forceinline__ void attn_tile(bool edge, const half_t* __restrict__ 
         const half2v pr = __builtin_convertvector(e2, half2v);
         pf[kb][r >> 3][r & 7] = pr[0];
         pf[kb][r >> 3][(r & 7) + 1] = pr[1];
-        psum0 += e2[0];
-        psum1 += e2[1];
+        // (the sums start from the first terms rather than from 0 + them: one add fewer each)
+        psum0 = kb == 0 && r == 0 ? e2[0] : psum0 + e2[0];
+        psum1 = kb == 0 && r == 0 ? e2[1] : psum1 + e2[1];
       }
     return psum0 + psum1;
   };
@@ -434,6 +435,35 @@ __device__ __forceinline__ void first_rows(const AttnArgs& a, int b, int h, floa
   }
 }
 
+// One step of the main loop: refill the other stage, process key tile kt from stage STAGE
+// (a constant, so every fragment address is a per-lane register plus a fixed offset), wait
+// for the copy and meet at the barrier.
+template <int DH, int MASK, bool DIRECT, int STAGE>
+__device__ __forceinline__ void key_tile(AttnSmem<DH>& sm, TileCopy<DH, DIRECT>& cp, const half_t* __restrict__ Kb,
+                                         const half_t* __restrict__ Vb, int kt, int kt1, int r0, int L, int window,
+                                         const half8 (&qf)[DH / 16], RowState<DH / 32>& st, floatx16& negm, int qrow,
+                                         int krow, int l32, int hf) {
+  const int k0 = kt * ABN;
+  const bool more = kt + 1 < kt1;
+  // The other stage was last read before the previous barrier: refill it now.
+  if (more) cp.issue(Kb, Vb, k0 + ABN, sm.k[STAGE ^ 1], sm.v[STAGE ^ 1]);
+  // A wave skips tiles that hold no visible key for any of its 32 rows; only tiles that
+  // cross a mask edge (for its rows) or the end of the sequence test keys.
+  bool edge = (k0 + ABN > L), act = true;
+  if (MASK != kMaskNone) {
+    act = k0 <= r0 + 31;
+    edge |= (k0 + ABN - 1 > r0);
+  }
+  if (MASK == kMaskWindow) {
+    act = act && (k0 + ABN - 1 > r0 - window);
+    edge |= (k0 <= r0 + 31 - window);
+  }
+  if (act) attn_tile<DH, MASK>(edge, sm.k[STAGE], sm.v[STAGE], qf, st, negm, k0, qrow, L, window, krow, l32, hf);
+  if (more) cp.commit(sm.k[STAGE ^ 1], sm.v[STAGE ^ 1]);
+  wait_global_loads();
+  __syncthreads();
+}
+
 template <int DH, int MASK, bool DIRECT>
 __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) AttnSmem<DH> sm;
@@ -517,27 +547,11 @@ __global__ __launch_bounds__(AThreads, 2) void attn_fwd_f16_kernel(AttnArgs a) {
   __syncthreads();
 
   const int krow = sigma_row(l32);
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int k0 = kt * ABN;
-    const int stage = (kt - kt0) & 1;
-    const bool more = kt + 1 < kt1;
-    // The other stage was last read before the previous barrier: refill it now.
-    if (more) cp.issue(Kb, Vb, k0 + ABN, sm.k[stage ^ 1], sm.v[stage ^ 1]);
-    // A wave skips tiles that hold no visible key for any of its 32 rows; only tiles that
-    // cross a mask edge (for its rows) or the end of the sequence test keys.
-    bool edge = (k0 + ABN > L), act = true;
-    if (MASK != kMaskNone) {
-      act = k0 <= r0 + 31;
-      edge |= (k0 + ABN - 1 > r0);
-    }
-    if (MASK == kMaskWindow) {
-      act = act && (k0 + ABN - 1 > r0 - window);
-      edge |= (k0 <= r0 + 31 - window);
-    }
-    if (act) attn_tile<DH, MASK>(edge, sm.k[stage], sm.v[stage], qf, st, negm, k0, qrow, L, window, krow, l32, hf);
-    if (more) cp.commit(sm.k[stage ^ 1], sm.v[stage ^ 1]);
-    wait_global_loads();
-    __syncthreads();
+  // Two key tiles per iteration, one per LDS stage, so that each tile's stage is a constant.
+  for (int kt = kt0; kt < kt1; kt += 2) {
+    key_tile<DH, MASK, DIRECT, 0>(sm, cp, Kb, Vb, kt, kt1, r0, L, window, qf, st, negm, qrow, krow, l32, hf);
+    if (kt + 1 < kt1)
+      key_tile<DH, MASK, DIRECT, 1>(sm, cp, Kb, Vb, kt + 1, kt1, r0, L, window, qf, st, negm, qrow, krow, l32, hf);
   }
 
   const float lt = st.l + __shfl_xor(st.l, 32);
