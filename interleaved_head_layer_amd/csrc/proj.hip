@@ -661,89 +661,208 @@ __device__ __forceinline__ void alpha_operands(const float* __restrict__ al, int
       }
 }
 
-// V~^T from Y_V^T.  A wave owns one channel c and 32*TQ tokens of one sequence: lane n (of
-// 32) loads TQ consecutive tokens TQ*n .. TQ*n + TQ-1, so column n of product block q is
-// token TQ*n + q; after the TQ blocks a lane holds, for each of its (h, j) rows, TQ
-// consecutive tokens, i.e. TQ*P consecutive fp16 of V~^T[b][h][c][*] (P in {1, 2, 4}).
-// TQ = 2 halves the registers of the large cases (more waves in flight).  grid
-// (ceil(M / (128 TQ)), d), 256 threads.
-template <int P, int MB, int KS, int TQ>
-__global__ __launch_bounds__(256) void mix_v_mfma_kernel(ProjArgs pa) {
-  typedef float floatq __attribute__((ext_vector_type(TQ)));
-  const int M = pa.B * pa.N, d = pa.d, H = pa.H, N = pa.N;
-  const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
-  // The four waves take consecutive blocks of one channel: 128*TQ*4 bytes runs per row.
-  const int c = blockIdx.y;
-  const int tok0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 32 * TQ;  // N % 128 == 0: one sequence
-  if (tok0 >= M) return;
-  const int b = tok0 / N, t0 = tok0 % N;
-  // B operands, blocks q < TQ: B[k][n] = Y_V^T[m = ks*16 + 8*hf + k%8][token TQ*n + q].
-  half8 bh[TQ][KS], bl[TQ][KS];
-  floatq yall[KS][8];
+// Q~/K~ from token-major Y on the matrix cores.  For one token the mixing is a product:
+// out[(h, j)][c] = sum_m alpha[m][h][j] Y[m][c], alpha^T (rows h*P + j, MB blocks of 32)
+// times the token's [H][d] block (KS k-steps of 16 source heads), with the same fp16 hi/lo
+// split as above (the vector-unit kernel above spends H*P*H*d fused multiply-adds per token
+// on the same result and is bound by them).  A work item is one token and one 64-channel half
+// of d; column n of product q is channel 64*half + 2n + q, so a lane loads two consecutive
+// channels of each source head at once.  The H*P x 64 fp16 result goes through the wave's own
+// LDS block and leaves as 16-byte stores, eight lanes per 128-byte row segment.  A wave walks
+// items gw, gw + nw, ... with the next item's loads in flight during the current one's
+// products.  Source heads m >= H read head 0 (finite) against zero alpha operands.  d in
+// {64, 128}, P in {1, 2, 4}; grid (x, nmat), 256 threads.
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+template <int MB, int KS, int P>
+__global__ __launch_bounds__(256, 2) void mix_qk_mfma_kernel(ProjArgs pa) {
+  constexpr int ORW = 64 + 8;  // staged row (halves): 144 bytes, so 32 rows' writes spread over the banks
+  __shared__ __attribute__((aligned(16))) half_t ost[4][MB * 32 * ORW];
+  const int which = blockIdx.y;
+  const int M = pa.B * pa.N, D = pa.D, d = pa.d, H = pa.H, N = pa.N, HP = H * P;
+  const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5, w = threadIdx.x >> 6;
+  const int yw = pa.ywidth > 0 ? pa.ywidth : 2;  // projected matrices per token row of Yqk
+  half_t* __restrict__ outb = which == 0 ? pa.Q : which == 1 ? pa.K : pa.Vrow;
+  float* __restrict__ oute = which == 0 ? pa.Qe : which == 1 ? pa.Ke : nullptr;
+  const float oscale = which == 0 ? pa.qscale : 1.f;  // Q leaves pre-scaled, in one rounding
+  const int halves = d / 64, nitems = M * halves, nw = gridDim.x * 4;
+  int item = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(w);
+  if (item >= nitems) return;
+  half_t* os = ost[w];
+  // B operand of product q, k-step ks: B[k][n] = Y[m = ks*16 + 8*hf + k%8][64*half + 2n + q].
+  int mrow[KS][8];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int m = ks * 16 + 8 * hf + e;
-      yall[ks][e] = *reinterpret_cast<const floatq*>(pa.Yvt + static_cast<int64_t>((m < H ? m : 0) * d + c) * M + tok0 + TQ * n);
+      mrow[ks][e] = (m < H ? m : 0) * d;
     }
+  auto load = [&](int it, floatx2 (&yv)[KS][8]) {
+    const int tk = it / halves, c0 = (it % halves) * 64;
+    const float* __restrict__ y = pa.Yqk + static_cast<int64_t>(tk) * yw * D + which * D + c0 + 2 * n;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) yv[ks][e] = *reinterpret_cast<const floatx2*>(y + mrow[ks][e]);
+  };
+  floatx2 yv[KS][8];
+  load(item, yv);
+  half8 ah[MB][KS], alo[MB][KS];
+  alpha_operands<MB, KS>(pa.alpha[which], H, P, ah, alo);
+  for (; item < nitems; item += nw) {
+    half8 bh[2][KS], bl[2][KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          bh[q][ks][e] = hi_f16(yv[ks][e][q]);
+          bl[q][ks][e] = lo_f16(yv[ks][e][q]);
+        }
+    if (item + nw < nitems) load(item + nw, yv);
+    const int tok = item / halves, c0 = (item % halves) * 64;
+    const int b = tok / N, t = tok % N;
+    const bool early = oute != nullptr && t * P < pa.R;  // wave-uniform, rare
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      floatx16 acc[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[q][r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          acc[q] = mfma32(ah[mb][ks], bh[q][ks], acc[q]);
+          acc[q] = mfma32(alo[mb][ks], bh[q][ks], acc[q]);
+          acc[q] = mfma32(ah[mb][ks], bl[q][ks], acc[q]);
+        }
+      }
+      // Lane rows: row = mb*32 + 8*(r/4) + 4*hf + r%4 = h*P + j.
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = mb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        const half2v v = {static_cast<half_t>(acc[0][r] * oscale), static_cast<half_t>(acc[1][r] * oscale)};
+        *reinterpret_cast<half2v*>(os + row * ORW + 2 * n) = v;
+      }
+      if (__builtin_expect(early, false)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = mb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const int h = row / P, j = row % P, i = t * P + j;
+          if (row < HP && i < pa.R) {
+            const floatx2 f = {acc[0][r], acc[1][r]};
+            *reinterpret_cast<floatx2*>(oute + (static_cast<int64_t>(b) * pa.R + i) * D + h * d + c0 + 2 * n) = f;
+          }
+        }
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // LDS in order within the wave
+    // Row (h, j) of the token: 64 channels at out[(tok*P + j)*D + h*d + c0], 8 chunks of 16 B.
+    half_t* __restrict__ out = outb + static_cast<int64_t>(tok) * P * D + c0;
+    for (int k = lane; k < HP * 8; k += 64) {
+      const int row = k >> 3, ch = k & 7;
+      const half8 v = *reinterpret_cast<const half8*>(os + row * ORW + ch * 8);
+      *reinterpret_cast<half8*>(out + (row % P) * D + (row / P) * d + ch * 8) = v;
+    }
+  }
+}
+
+// V~^T from Y_V^T.  A work item is one channel c and 32*TQ tokens of one sequence: lane n
+// (of 32) loads TQ consecutive tokens TQ*n .. TQ*n + TQ-1, so column n of product block q is
+// token TQ*n + q; after the TQ blocks a lane holds, for each of its (h, j) rows, TQ
+// consecutive tokens, i.e. TQ*P consecutive fp16 of V~^T[b][h][c][*] (P in {1, 2, 4}).  A
+// wave walks items gw, gw + nw, ... (alpha's operands built once, the next item's loads in
+// flight during the current one's products); consecutive waves take consecutive token blocks
+// of one channel.  TQ = 2 halves the registers of the large cases.  Needs N % (32 TQ) == 0.
+template <int P, int MB, int KS, int TQ>
+__global__ __launch_bounds__(256, 2) void mix_v_mfma_kernel(ProjArgs pa) {
+  typedef float floatq __attribute__((ext_vector_type(TQ)));
+  const int M = pa.B * pa.N, d = pa.d, H = pa.H, N = pa.N;
+  const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
+  const int nblk = M / (32 * TQ), nitems = nblk * d, nw = gridDim.x * 4;
+  int item = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (item >= nitems) return;
+  // B operands, blocks q < TQ: B[k][n] = Y_V^T[m = ks*16 + 8*hf + k%8][token TQ*n + q]; source
+  // heads m >= H read head 0 (finite) against zero alpha operands.
+  int64_t mrow[KS][8];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int m = ks * 16 + 8 * hf + e;
+      mrow[ks][e] = static_cast<int64_t>(m < H ? m : 0) * d * M;
+    }
+  auto load = [&](int it, floatq (&y)[KS][8]) {
+    const int c = it / nblk, tok0 = (it % nblk) * 32 * TQ;
+    const float* __restrict__ src = pa.Yvt + static_cast<int64_t>(c) * M + tok0 + TQ * n;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[ks][e] = *reinterpret_cast<const floatq*>(src + mrow[ks][e]);
+  };
+  floatq yall[KS][8];
+  load(item, yall);
   half8 ah[MB][KS], alo[MB][KS];
   alpha_operands<MB, KS>(pa.alpha[2], H, P, ah, alo);
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-    for (int q = 0; q < TQ; ++q)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int m = ks * 16 + 8 * hf + e;
-        const float y = m < H ? yall[ks][e][q] : 0.f;
-        bh[q][ks][e] = hi_f16(y);
-        bl[q][ks][e] = lo_f16(y);
-      }
-  }
   const int64_t L = static_cast<int64_t>(P) * N;
   const int HP = H * P;
+  for (; item < nitems; item += nw) {
+    half8 bh[TQ][KS], bl[TQ][KS];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    floatx16 acc[TQ];
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-    for (int q = 0; q < TQ; ++q) {
+      for (int q = 0; q < TQ; ++q)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[q][r] = 0.f;
+        for (int e = 0; e < 8; ++e) {
+          bh[q][ks][e] = hi_f16(yall[ks][e][q]);
+          bl[q][ks][e] = lo_f16(yall[ks][e][q]);
+        }
+    if (item + nw < nitems) load(item + nw, yall);
+    const int c = item / nblk, tok0 = (item % nblk) * 32 * TQ;
+    const int b = tok0 / N, t0 = tok0 % N;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        acc[q] = mfma32(ah[mb][ks], bh[q][ks], acc[q]);
-        acc[q] = mfma32(alo[mb][ks], bh[q][ks], acc[q]);
-        acc[q] = mfma32(ah[mb][ks], bl[q][ks], acc[q]);
+    for (int mb = 0; mb < MB; ++mb) {
+      floatx16 acc[TQ];
+#pragma unroll
+      for (int q = 0; q < TQ; ++q) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[q][r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          acc[q] = mfma32(ah[mb][ks], bh[q][ks], acc[q]);
+          acc[q] = mfma32(alo[mb][ks], bh[q][ks], acc[q]);
+          acc[q] = mfma32(ah[mb][ks], bl[q][ks], acc[q]);
+        }
       }
-    }
-    // Lane rows: row = mb*32 + 8*(r/4) + 4*hf + r%4 = h*P + j.
+      // Lane rows: row = mb*32 + 8*(r/4) + 4*hf + r%4 = h*P + j.
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {        // g = r / 4: rows 4*(2g + hf) .. +3
-      const int row0 = mb * 32 + 8 * g + 4 * hf;
-      if (row0 >= HP) continue;
+      for (int g = 0; g < 4; ++g) {        // g = r / 4: rows 4*(2g + hf) .. +3
+        const int row0 = mb * 32 + 8 * g + 4 * hf;
+        if (row0 >= HP) continue;
 #pragma unroll
-      for (int u = 0; u < 4 / P; ++u) {  // heads among these 4 rows
-        const int h = (row0 + u * P) / P;
-        if (h >= H) continue;
-        // TQ tokens x P pseudo-tokens of head h, stacked positions (t0 + TQ*n + q)*P + j
-        typedef _Float16 halfv __attribute__((ext_vector_type(TQ * P)));
-        halfv v;
-#pragma unroll
-        for (int q = 0; q < TQ; ++q)
-#pragma unroll
-          for (int j = 0; j < P; ++j) v[q * P + j] = static_cast<half_t>(acc[q][4 * g + u * P + j]);
-        half_t* dst = pa.Vt + (static_cast<int64_t>(b * H + h) * d + c) * L + static_cast<int64_t>(t0 + TQ * n) * P;
-        *reinterpret_cast<halfv*>(dst) = v;
-        if (pa.Ve && (t0 + TQ * n) * P < pa.R) {
-          float* erow = pa.Ve + static_cast<int64_t>(b) * pa.R * pa.D + h * d + c;
+        for (int u = 0; u < 4 / P; ++u) {  // heads among these 4 rows
+          const int h = (row0 + u * P) / P;
+          if (h >= H) continue;
+          // TQ tokens x P pseudo-tokens of head h, stacked positions (t0 + TQ*n + q)*P + j
+          typedef _Float16 halfv __attribute__((ext_vector_type(TQ * P)));
+          halfv v;
 #pragma unroll
           for (int q = 0; q < TQ; ++q)
 #pragma unroll
-            for (int j = 0; j < P; ++j) {
-              const int i = (t0 + TQ * n + q) * P + j;
-              if (i < pa.R) erow[static_cast<int64_t>(i) * pa.D] = acc[q][4 * g + u * P + j];
-            }
+            for (int j = 0; j < P; ++j) v[q * P + j] = static_cast<half_t>(acc[q][4 * g + u * P + j]);
+          half_t* dst = pa.Vt + (static_cast<int64_t>(b * H + h) * d + c) * L + static_cast<int64_t>(t0 + TQ * n) * P;
+          *reinterpret_cast<halfv*>(dst) = v;
+          if (pa.Ve && (t0 + TQ * n) * P < pa.R) {
+            float* erow = pa.Ve + static_cast<int64_t>(b) * pa.R * pa.D + h * d + c;
+#pragma unroll
+            for (int q = 0; q < TQ; ++q)
+#pragma unroll
+              for (int j = 0; j < P; ++j) {
+                const int i = (t0 + TQ * n + q) * P + j;
+                if (i < pa.R) erow[static_cast<int64_t>(i) * pa.D] = acc[q][4 * g + u * P + j];
+              }
+          }
         }
       }
     }
@@ -752,14 +871,24 @@ __global__ __launch_bounds__(256) void mix_v_mfma_kernel(ProjArgs pa) {
 
 template <int P>
 bool launch_mix_v_mfma_p(const ProjArgs& pa, hipStream_t s) {
-  const int M = pa.B * pa.N;
+  const int64_t M = static_cast<int64_t>(pa.B) * pa.N;
   const int mb = (pa.H * P + 31) / 32, ks = (pa.H + 15) / 16;
-  const dim3 g4((M + 511) / 512, pa.d), g2((M + 255) / 256, pa.d);
-  if (mb == 1 && ks == 1) hipLaunchKernelGGL((mix_v_mfma_kernel<P, 1, 1, 4>), g4, dim3(256), 0, s, pa);
-  else if (mb <= 2 && ks == 1) hipLaunchKernelGGL((mix_v_mfma_kernel<P, 2, 1, 4>), g4, dim3(256), 0, s, pa);
-  else if (mb <= 3 && ks <= 2) hipLaunchKernelGGL((mix_v_mfma_kernel<P, 3, 2, 2>), g2, dim3(256), 0, s, pa);
-  else if (mb <= 4 && ks <= 2) hipLaunchKernelGGL((mix_v_mfma_kernel<P, 4, 2, 2>), g2, dim3(256), 0, s, pa);
-  else return false;
+  const dim3 g4(static_cast<unsigned>(std::min<int64_t>((M / 128 * pa.d + 3) / 4, 1024))),
+      g2(static_cast<unsigned>(std::min<int64_t>((M / 64 * pa.d + 3) / 4, 1024)));
+  // With H <= 16 (one k-step) H*P <= 64; with two k-steps P = 1 needs one row block, P = 2 two.
+  if (ks == 1) {
+    if (mb == 1) hipLaunchKernelGGL((mix_v_mfma_kernel<P, 1, 1, 4>), g4, dim3(256), 0, s, pa);
+    else if constexpr (P >= 2) hipLaunchKernelGGL((mix_v_mfma_kernel<P, 2, 1, 4>), g4, dim3(256), 0, s, pa);
+    return true;
+  }
+  if (mb == 1) hipLaunchKernelGGL((mix_v_mfma_kernel<P, 1, 2, 2>), g2, dim3(256), 0, s, pa);
+  else if constexpr (P >= 2) {
+    if (mb == 2) hipLaunchKernelGGL((mix_v_mfma_kernel<P, 2, 2, 2>), g2, dim3(256), 0, s, pa);
+    else if constexpr (P == 4) {
+      if (mb == 3) hipLaunchKernelGGL((mix_v_mfma_kernel<P, 3, 2, 2>), g2, dim3(256), 0, s, pa);
+      else hipLaunchKernelGGL((mix_v_mfma_kernel<P, 4, 2, 2>), g2, dim3(256), 0, s, pa);
+    }
+  }
   return true;
 }
 
@@ -773,6 +902,35 @@ bool launch_mix_v_mfma(const ProjArgs& pa, hipStream_t s) {
   }
 }
 
+template <int MB, int KS, int P>
+void launch_mix_qk_mfma_mk(const ProjArgs& pa, int nmat, hipStream_t s) {
+  const int64_t items = static_cast<int64_t>(pa.B) * pa.N * (pa.d / 64);
+  const dim3 grid(static_cast<unsigned>(std::min<int64_t>((items + 3) / 4, 1024)), nmat);
+  hipLaunchKernelGGL((mix_qk_mfma_kernel<MB, KS, P>), grid, dim3(256), 0, s, pa);
+}
+
+template <int KS>
+bool launch_mix_qk_mfma_k(const ProjArgs& pa, int nmat, hipStream_t s) {
+  const int mb = (pa.H * pa.P + 31) / 32;
+  switch (pa.P * 8 + mb) {
+    case 1 * 8 + 1: launch_mix_qk_mfma_mk<1, KS, 1>(pa, nmat, s); return true;
+    case 2 * 8 + 1: launch_mix_qk_mfma_mk<1, KS, 2>(pa, nmat, s); return true;
+    case 2 * 8 + 2: launch_mix_qk_mfma_mk<2, KS, 2>(pa, nmat, s); return true;
+    case 4 * 8 + 1: launch_mix_qk_mfma_mk<1, KS, 4>(pa, nmat, s); return true;
+    case 4 * 8 + 2: launch_mix_qk_mfma_mk<2, KS, 4>(pa, nmat, s); return true;
+    case 4 * 8 + 3: launch_mix_qk_mfma_mk<3, KS, 4>(pa, nmat, s); return true;
+    case 4 * 8 + 4: launch_mix_qk_mfma_mk<4, KS, 4>(pa, nmat, s); return true;
+    default: return false;
+  }
+}
+
+// Q~/K~ (and the row-major V~) mixing on the matrix cores when d is 64 or 128, H <= 32,
+// H*P <= 128 and P is 1, 2 or 4; false otherwise (the caller then uses the vector-unit kernel).
+bool launch_mix_qk_mfma(const ProjArgs& pa, int nmat, hipStream_t s) {
+  if ((pa.d != 64 && pa.d != 128) || pa.H > 32 || pa.H * pa.P > 128) return false;
+  return pa.H <= 16 ? launch_mix_qk_mfma_k<1>(pa, nmat, s) : launch_mix_qk_mfma_k<2>(pa, nmat, s);
+}
+
 template <int HMAX>
 void launch_mix(const ProjArgs& pa, hipStream_t s) {
   constexpr int CW = HMAX <= 20 ? 4 : HMAX <= 32 ? 2 : 1;
@@ -780,7 +938,8 @@ void launch_mix(const ProjArgs& pa, hipStream_t s) {
   const int64_t M = static_cast<int64_t>(pa.B) * pa.N;
   const size_t lds = static_cast<size_t>(pa.H) * pa.P * HMAX * sizeof(float);
   const int64_t nqk = M * (pa.d / CW);
-  hipLaunchKernelGGL((mix_qk_kernel<HMAX, CW>), dim3(static_cast<unsigned>((nqk + 255) / 256), 2), dim3(256), lds, s, pa);
+  if (!launch_mix_qk_mfma(pa, 2, s))
+    hipLaunchKernelGGL((mix_qk_kernel<HMAX, CW>), dim3(static_cast<unsigned>((nqk + 255) / 256), 2), dim3(256), lds, s, pa);
   if (launch_mix_v_mfma(pa, s)) return;
   const int64_t nv = (M + TW - 1) / TW;
   hipLaunchKernelGGL((mix_v_kernel<HMAX, TW>), dim3(static_cast<unsigned>((nv + 255) / 256), pa.d), dim3(256), lds, s, pa);
@@ -788,6 +947,7 @@ void launch_mix(const ProjArgs& pa, hipStream_t s) {
 
 template <int HMAX>
 void launch_mix_rows(const ProjArgs& pa, int nmat, hipStream_t s) {
+  if (launch_mix_qk_mfma(pa, nmat, s)) return;
   constexpr int CW = HMAX <= 20 ? 4 : HMAX <= 32 ? 2 : 1;
   const int64_t M = static_cast<int64_t>(pa.B) * pa.N;
   const size_t lds = static_cast<size_t>(pa.H) * pa.P * HMAX * sizeof(float);
