@@ -176,6 +176,11 @@ __device__ __forceinline__ void attn_tile(bool edge, const half_t* __restrict__ 
   constexpr int NKS = DH / 16, NCB = DH / 32;
   // K fragments i = kstep * 2 + kb, read kPre ahead of their product; the first kPre V^T
   // fragments are read after the score product so they arrive during the softmax.
+  // Wave priority: the softmax runs at 0; each product phase starts at 1 (score) or 0 (PV)
+  // and rises to 3 halfway, so of the two waves sharing a SIMD the one further into its
+  // products keeps the matrix core and the other's products wait.  The waves then drift
+  // into opposite phases (one's softmax under the other's products) instead of running
+  // their products and their softmax at the same time.
   constexpr int NK = 2 * NKS, kPre = 4;
   auto kfrag = [&](int i) {
     const int kr_ = (i & 1) * 32 + krow;
@@ -191,18 +196,30 @@ __device__ __forceinline__ void attn_tile(bool edge, const half_t* __restrict__ 
   for (int i = 0; i < kPre; ++i) kr[i] = kfrag(i);
   __builtin_amdgcn_sched_barrier(0); __builtin_amdgcn_s_setprio(1); __builtin_amdgcn_sched_barrier(0);
   floatx16 s[2];
+  constexpr int HK = NK / 2;
 #pragma unroll
-  for (int i = 0; i < NK; ++i) {
-    if (i + kPre < NK) kr[i + kPre] = kfrag(i + kPre);
+  for (int i = 0; i < HK; ++i) {
+    kr[i + kPre] = kfrag(i + kPre);
     s[i & 1] = mfma32(kr[i], qf[i >> 1], i < 2 ? negm : s[i & 1]);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+#pragma unroll
+  for (int i = 0; i < HK; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0); __builtin_amdgcn_s_setprio(3); __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = HK; i < NK; ++i) {
+    if (i + kPre < NK) kr[i + kPre] = kfrag(i + kPre);
+    s[i & 1] = mfma32(kr[i], qf[i >> 1], s[i & 1]);
   }
   constexpr int NV = 4 * NCB;
   half8 vr[NV];
 #pragma unroll
   for (int j = 0; j < kPre; ++j) vr[j] = vfrag(j);
-  __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
 #pragma unroll
-  for (int i = 0; i < NK; ++i) {
+  for (int i = HK; i < NK; ++i) {
     if (i + kPre < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   }
@@ -283,15 +300,28 @@ __device__ __forceinline__ void attn_tile(bool edge, const half_t* __restrict__ 
     tsum = probs();
   }
   st.l += tsum;
-  __builtin_amdgcn_sched_barrier(0); __builtin_amdgcn_s_setprio(1); __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_sched_barrier(0); __builtin_amdgcn_s_setprio(0); __builtin_amdgcn_sched_barrier(0);
+  constexpr int HV = NV / 2;
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
+  for (int j = 0; j < HV; ++j) {
+    vr[j + kPre] = vfrag(j + kPre);
+    const int ks2 = j / NCB;
+    st.o[j % NCB] = mfma32(vr[j], pf[ks2 >> 1][ks2 & 1], st.o[j % NCB]);
+  }
+#pragma unroll
+  for (int j = 0; j < HV; ++j) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0); __builtin_amdgcn_s_setprio(3); __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = HV; j < NV; ++j) {
     if (j + kPre < NV) vr[j + kPre] = vfrag(j + kPre);
     const int ks2 = j / NCB;
     st.o[j % NCB] = mfma32(vr[j], pf[ks2 >> 1][ks2 & 1], st.o[j % NCB]);
   }
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
+  for (int j = HV; j < NV; ++j) {
     if (j + kPre < NV) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   }
