@@ -581,14 +581,30 @@ __device__ __forceinline__ void bwd_split_body(const AttnBwdArgs& a, SplitSmem<D
         if (PART) dp = mfma32(*reinterpret_cast<const half8*>(sm.g[st] + off), vf[k], dp);
       }
       // Lane (l32, hf), accumulator r: key krow, query q0 + 16*hf + r.  PART 0 keeps the
-      // probabilities, PART 1 dS = A * (dA - D).
+      // probabilities, PART 1 dS = A * (dA - D).  A tile that crosses a mask edge or the
+      // sequence end first sets the scores of the queries that do not see the key to -inf (one
+      // unsigned range test each), so that the loop below runs without branches; queries past
+      // the end have lse = +inf.  The lane's 16 lse (and D) values are four 16-byte LDS reads.
+      if (edge) {
+        const int base = q0 + 16 * hf;
+        const int lo = max(MASK != kMaskNone ? krow - base : 0, 0);
+        const int last = (MASK == kMaskWindow ? min(krow + window - 1, L - 1) : L - 1) - base;
+        const unsigned n = krow < L ? static_cast<unsigned>(max(min(last, 15) + 1 - lo, 0)) : 0u;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (static_cast<unsigned>(r - lo) >= n) s[r] = -__builtin_inff();
+      }
+      floatx4 lq[4], dq4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        lq[u] = *reinterpret_cast<const floatx4*>(&sm.ls[st][16 * hf + 4 * u]);
+        if (PART) dq4[u] = *reinterpret_cast<const floatx4*>(&sm.ds[st][16 * hf + 4 * u]);
+      }
       half8 pf[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int qi = 16 * hf + r;
-        float v = fast_exp2(s[r] - sm.ls[st][qi]);
-        if (PART) v *= dp[r] - sm.ds[st][qi];
-        if (edge && !seen<MASK>(q0 + qi, krow, L, window)) v = 0.f;
+        float v = fast_exp2(s[r] - lq[r >> 2][r & 3]);
+        if (PART) v *= dp[r] - dq4[r >> 2][r & 3];
         pf[r >> 3][r & 7] = static_cast<half_t>(v);
       }
       // dV^T += dO^T A  or  dK^T += (Q*scale)^T dS.
@@ -740,14 +756,23 @@ __device__ __forceinline__ void bwd_dq_direct_body(const AttnBwdArgs& a, DqSmem<
         s = mfma32(*reinterpret_cast<const half8*>(sm.k[st] + off), qf[k], s);
         dp = mfma32(*reinterpret_cast<const half8*>(sm.v[st] + off), gf[k], dp);
       }
-      // Lane (l32, hf), accumulator r: query qrow, key k0 + 16*hf + r.
+      // Lane (l32, hf), accumulator r: query qrow, key k0 + 16*hf + r.  A tile that crosses a
+      // mask edge or the sequence end first sets the scores of the keys the row does not see to
+      // -inf (one unsigned range test each: keys lo .. lo + n - 1 of the lane's 16 are seen),
+      // so that the loop below runs without branches; a row past the end has lse = +inf.
+      if (edge) {
+        const int base = k0 + 16 * hf;
+        const int last = (MASK == kMaskNone ? L - 1 : min(qrow, L - 1)) - base;
+        const int lo = max(MASK == kMaskWindow ? qrow - window + 1 - base : 0, 0);
+        const unsigned n = static_cast<unsigned>(max(min(last, 15) + 1 - lo, 0));
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (static_cast<unsigned>(r - lo) >= n) s[r] = -__builtin_inff();
+      }
       half8 dsf[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float g = fast_exp2(s[r] - lse) * (dp[r] - dd);
-        if (edge && !seen<MASK>(qrow, k0 + 16 * hf + r, L, window)) g = 0.f;
-        dsf[r >> 3][r & 7] = static_cast<half_t>(g);
-      }
+      for (int r = 0; r < 16; ++r)
+        dsf[r >> 3][r & 7] = static_cast<half_t>(fast_exp2(s[r] - lse) * (dp[r] - dd));
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
