@@ -18,6 +18,8 @@
 //    dV^T += dO^T A and dK^T += Q^T dS.
 // The operand that is contracted over in the second product needs the other orientation, so
 // a prep kernel writes channel-major copies of Q, K, V and dO once.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -554,11 +556,20 @@ __device__ __forceinline__ void bwd_split_body(const AttnBwdArgs& a, SplitSmem<D
   }
   __syncthreads();
   const int qr = sigma(l32);
-  for (int qti = qt0; qti < qt1; ++qti) {
-    const int q0 = qti * QTile, st = (qti - qt0) & 1;
+  // One query tile from LDS stage ST (a constant: every fragment address is a per-lane
+  // register plus a fixed offset; the loop below takes two tiles per iteration).  The score
+  // products' A fragments (Q*scale rows, and dO rows for dK, alternating) and the transposed
+  // tile's fragments are read kPre products ahead of use, the first kPre of the latter during
+  // the exponentials (dV, at three workgroups per CU, reads two ahead to stay in its registers).
+  // Both product phases run at wave priority 2, rising to 3 halfway (the exponentials at 0):
+  // the wave further into its products keeps the matrix core.
+  constexpr int kPre = PART ? 4 : 2, NA = PART ? 2 * NKS : NKS, NT = 2 * NCB;
+  auto tile = [&](int qti, auto stc) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stc)::value;
+    const int q0 = qti * QTile;
     const bool more = qti + 1 < qt1;
     if (more) {
-      issue(q0 + QTile, st ^ 1);
+      issue(q0 + QTile, ST ^ 1);
       load_ld(q0 + QTile);
     }
     bool act = true, edge = q0 + QTile > L || kw0 + 32 > L;
@@ -571,15 +582,50 @@ __device__ __forceinline__ void bwd_split_body(const AttnBwdArgs& a, SplitSmem<D
       edge |= q0 + QTile - 1 >= kw0 + window;
     }
     if (act) {
+      auto afrag = [&](int i) {
+        const int k = PART ? i >> 1 : i;
+        const half_t* base = (PART && (i & 1)) ? sm.g[ST] : sm.q[ST];
+        return *reinterpret_cast<const half8*>(base + qr * DH + ((2 * k + hf) ^ rswz<DH>(qr)) * 8);
+      };
+      auto tfrag = [&](int j) {  // j = cb * 2 + s2
+        const int c = (j >> 1) * 32 + l32;
+        return *reinterpret_cast<const half8*>(sm.t[ST] + c * QTile + ((2 * hf + (j & 1)) ^ tswz(c)) * 8);
+      };
       floatx16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+      half8 fa[NA];
 #pragma unroll
-      for (int k = 0; k < NKS; ++k) {
-        const int off = qr * DH + ((2 * k + hf) ^ rswz<DH>(qr)) * 8;
-        s = mfma32(*reinterpret_cast<const half8*>(sm.q[st] + off), kf[k], s);
-        if (PART) dp = mfma32(*reinterpret_cast<const half8*>(sm.g[st] + off), vf[k], dp);
+      for (int i = 0; i < kPre; ++i) fa[i] = afrag(i);
+      __builtin_amdgcn_sched_barrier(0); __builtin_amdgcn_s_setprio(2); __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NA / 2; ++i) {
+        fa[i + kPre] = afrag(i + kPre);
+        if (PART && (i & 1)) dp = mfma32(fa[i], vf[i >> 1], dp);
+        else s = mfma32(fa[i], kf[PART ? i >> 1 : i], s);
       }
+#pragma unroll
+      for (int i = 0; i < NA / 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0); __builtin_amdgcn_s_setprio(3); __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = NA / 2; i < NA; ++i) {
+        if (i + kPre < NA) fa[i + kPre] = afrag(i + kPre);
+        if (PART && (i & 1)) dp = mfma32(fa[i], vf[i >> 1], dp);
+        else s = mfma32(fa[i], kf[PART ? i >> 1 : i], s);
+      }
+      half8 ft[NT];
+#pragma unroll
+      for (int j = 0; j < kPre; ++j) ft[j] = tfrag(j);
+#pragma unroll
+      for (int i = NA / 2; i < NA; ++i) {
+        if (i + kPre < NA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+      __builtin_amdgcn_sched_barrier(0); __builtin_amdgcn_s_setprio(0); __builtin_amdgcn_sched_barrier(0);
       // Lane (l32, hf), accumulator r: key krow, query q0 + 16*hf + r.  PART 0 keeps the
       // probabilities, PART 1 dS = A * (dA - D).  A tile that crosses a mask edge or the
       // sequence end first sets the scores of the queries that do not see the key to -inf (one
@@ -597,8 +643,8 @@ __device__ __forceinline__ void bwd_split_body(const AttnBwdArgs& a, SplitSmem<D
       floatx4 lq[4], dq4[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        lq[u] = *reinterpret_cast<const floatx4*>(&sm.ls[st][16 * hf + 4 * u]);
-        if (PART) dq4[u] = *reinterpret_cast<const floatx4*>(&sm.ds[st][16 * hf + 4 * u]);
+        lq[u] = *reinterpret_cast<const floatx4*>(&sm.ls[ST][16 * hf + 4 * u]);
+        if (PART) dq4[u] = *reinterpret_cast<const floatx4*>(&sm.ds[ST][16 * hf + 4 * u]);
       }
       half8 pf[2];
 #pragma unroll
@@ -608,20 +654,40 @@ __device__ __forceinline__ void bwd_split_body(const AttnBwdArgs& a, SplitSmem<D
         pf[r >> 3][r & 7] = static_cast<half_t>(v);
       }
       // dV^T += dO^T A  or  dK^T += (Q*scale)^T dS.
+      __builtin_amdgcn_sched_barrier(0); __builtin_amdgcn_s_setprio(2); __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
+      for (int j = 0; j < NT / 2; ++j) {
+        if (j + kPre < NT) ft[j + kPre] = tfrag(j + kPre);
+        acc[j >> 1] = mfma32(ft[j], pf[j & 1], acc[j >> 1]);
+      }
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const int c = cb * 32 + l32, off = c * QTile + ((2 * hf + s2) ^ tswz(c)) * 8;
-          acc[cb] = mfma32(*reinterpret_cast<const half8*>(sm.t[st] + off), pf[s2], acc[cb]);
-        }
+      for (int j = 0; j < NT / 2; ++j) {
+        if (j + kPre < NT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0); __builtin_amdgcn_s_setprio(3); __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = NT / 2; j < NT; ++j) {
+        if (j + kPre < NT) ft[j + kPre] = tfrag(j + kPre);
+        acc[j >> 1] = mfma32(ft[j], pf[j & 1], acc[j >> 1]);
+      }
+#pragma unroll
+      for (int j = NT / 2; j < NT; ++j) {
+        if (j + kPre < NT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0); __builtin_amdgcn_s_setprio(0); __builtin_amdgcn_sched_barrier(0);
     }
     wait_vmem();
     if (more && tid < QTile) {
-      sm.ls[st ^ 1][tid] = pl;
-      sm.ds[st ^ 1][tid] = pd;
+      sm.ls[ST ^ 1][tid] = pl;
+      sm.ds[ST ^ 1][tid] = pd;
     }
     __syncthreads();
+  };
+  for (int qti = qt0; qti < qt1; qti += 2) {
+    tile(qti, std::integral_constant<int, 0>{});
+    if (qti + 1 < qt1) tile(qti + 1, std::integral_constant<int, 1>{});
   }
   if (krow < L) {
     float* dst = (PART ? a.dK : a.dV) + rbase + static_cast<int64_t>(krow) * rs;
@@ -734,9 +800,15 @@ __device__ __forceinline__ void bwd_dq_direct_body(const AttnBwdArgs& a, DqSmem<
   wait_vmem();
   __syncthreads();
   const int kr = sigma(l32);
-  for (int kti = kt0; kti < kt1; ++kti) {
-    const int k0 = kti * KT32, st = (kti - kt0) & 1;
-    if (kti + 1 < kt1) issue(k0 + KT32, st ^ 1);
+  // One key tile from LDS stage ST (a constant; two tiles per iteration below).  The score
+  // products' A fragments (K rows and V rows, alternating) and the K^T fragments are read
+  // kPre products ahead of use, the first kPre K^T fragments during the exponentials.  Wave
+  // priority as in the dK and dV kernels.
+  constexpr int kPre = 4, NA = 2 * NKS, NT = 2 * NCB;
+  auto tile = [&](int kti, auto stc) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stc)::value;
+    const int k0 = kti * KT32;
+    if (kti + 1 < kt1) issue(k0 + KT32, ST ^ 1);
     bool act = true, edge = k0 + KT32 > L || r0 + 32 > L;
     if (MASK != kMaskNone) {
       act = k0 <= r0 + 31;
@@ -747,15 +819,49 @@ __device__ __forceinline__ void bwd_dq_direct_body(const AttnBwdArgs& a, DqSmem<
       edge |= k0 <= r0 + 31 - window;
     }
     if (act) {
+      auto afrag = [&](int i) {
+        const half_t* base = (i & 1) ? sm.v[ST] : sm.k[ST];
+        return *reinterpret_cast<const half8*>(base + kr * DH + ((2 * (i >> 1) + hf) ^ rswz<DH>(kr)) * 8);
+      };
+      auto tfrag = [&](int j) {  // j = s2 * NCB + cb
+        const int c = (j % NCB) * 32 + l32;
+        return *reinterpret_cast<const half8*>(sm.kt[ST] + c * KT32 + ((2 * hf + j / NCB) ^ tswz(c)) * 8);
+      };
       floatx16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+      half8 fa[NA];
 #pragma unroll
-      for (int k = 0; k < NKS; ++k) {
-        const int off = kr * DH + ((2 * k + hf) ^ rswz<DH>(kr)) * 8;
-        s = mfma32(*reinterpret_cast<const half8*>(sm.k[st] + off), qf[k], s);
-        dp = mfma32(*reinterpret_cast<const half8*>(sm.v[st] + off), gf[k], dp);
+      for (int i = 0; i < kPre; ++i) fa[i] = afrag(i);
+      __builtin_amdgcn_sched_barrier(0); __builtin_amdgcn_s_setprio(2); __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NA / 2; ++i) {
+        fa[i + kPre] = afrag(i + kPre);
+        if (i & 1) dp = mfma32(fa[i], gf[i >> 1], dp);
+        else s = mfma32(fa[i], qf[i >> 1], s);
       }
+#pragma unroll
+      for (int i = 0; i < NA / 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0); __builtin_amdgcn_s_setprio(3); __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = NA / 2; i < NA; ++i) {
+        if (i + kPre < NA) fa[i + kPre] = afrag(i + kPre);
+        if (i & 1) dp = mfma32(fa[i], gf[i >> 1], dp);
+        else s = mfma32(fa[i], qf[i >> 1], s);
+      }
+      half8 ft[NT];
+#pragma unroll
+      for (int j = 0; j < kPre; ++j) ft[j] = tfrag(j);
+#pragma unroll
+      for (int i = NA / 2; i < NA; ++i) {
+        if (i + kPre < NA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, kPre, 0);
+      __builtin_amdgcn_sched_barrier(0); __builtin_amdgcn_s_setprio(0); __builtin_amdgcn_sched_barrier(0);
       // Lane (l32, hf), accumulator r: query qrow, key k0 + 16*hf + r.  A tile that crosses a
       // mask edge or the sequence end first sets the scores of the keys the row does not see to
       // -inf (one unsigned range test each: keys lo .. lo + n - 1 of the lane's 16 are seen),
@@ -773,16 +879,36 @@ __device__ __forceinline__ void bwd_dq_direct_body(const AttnBwdArgs& a, DqSmem<
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         dsf[r >> 3][r & 7] = static_cast<half_t>(fast_exp2(s[r] - lse) * (dp[r] - dd));
+      __builtin_amdgcn_sched_barrier(0); __builtin_amdgcn_s_setprio(2); __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
+      for (int j = 0; j < NT / 2; ++j) {
+        if (j + kPre < NT) ft[j + kPre] = tfrag(j + kPre);
+        acc[j % NCB] = mfma32(ft[j], dsf[j / NCB], acc[j % NCB]);
+      }
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const int c = cb * 32 + l32, off = c * KT32 + ((2 * hf + s2) ^ tswz(c)) * 8;
-          acc[cb] = mfma32(*reinterpret_cast<const half8*>(sm.kt[st] + off), dsf[s2], acc[cb]);
-        }
+      for (int j = 0; j < NT / 2; ++j) {
+        if (j + kPre < NT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0); __builtin_amdgcn_s_setprio(3); __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = NT / 2; j < NT; ++j) {
+        if (j + kPre < NT) ft[j + kPre] = tfrag(j + kPre);
+        acc[j % NCB] = mfma32(ft[j], dsf[j / NCB], acc[j % NCB]);
+      }
+#pragma unroll
+      for (int j = NT / 2; j < NT; ++j) {
+        if (j + kPre < NT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0); __builtin_amdgcn_s_setprio(0); __builtin_amdgcn_sched_barrier(0);
     }
     wait_vmem();
     __syncthreads();
+  };
+  for (int kti = kt0; kti < kt1; kti += 2) {
+    tile(kti, std::integral_constant<int, 0>{});
+    if (kti + 1 < kt1) tile(kti + 1, std::integral_constant<int, 1>{});
   }
   if (qrow < L) {
     float* dst = a.dQ + rbase + static_cast<int64_t>(qrow) * rs;
