@@ -91,8 +91,9 @@ __global__ __launch_bounds__(BThreads) void bwd_prep_kernel(AttnBwdArgs a) {
     half_t* dst = t == 0 ? a.QsT : t == 1 ? a.KT : t == 2 ? a.VT : a.dOT;
     const int ld = t == 2 ? L : a.Lp;
     half_t* base = dst + static_cast<int64_t>(b * H + h) * DH * ld;
+    // Eight consecutive lanes write one channel's 64 positions (128 contiguous bytes).
     for (int idx = threadIdx.x; idx < DH * 8; idx += BThreads) {
-      const int c = idx % DH, u = idx / DH, l = l0 + 8 * u;
+      const int c = idx / 8, u = idx % 8, l = l0 + 8 * u;
       if (l >= ld) continue;
       half8 w;
 #pragma unroll
