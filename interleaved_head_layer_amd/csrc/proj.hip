@@ -197,6 +197,7 @@ __device__ __forceinline__ void gemm_tile(const NtArgs& g, NtSmem<RBW>& sm, Epi&
   epi(acc, i0, j0, wm, wn);
 }
 
+static_assert(GWaves * 64 * 64 * sizeof(float) <= sizeof(NtSmem<GRBW>), "epilogue staging");
 __global__ __launch_bounds__(GThreads, 1) void gemm_nt_bf16_kernel(NtArgs g) {
   __shared__ __attribute__((aligned(16))) NtSmem<GRBW> sm;
   if (gridDim.y > 1 || gridDim.z > 1) {  // batched launch: product blockIdx.y, K part blockIdx.z
@@ -210,7 +211,48 @@ __global__ __launch_bounds__(GThreads, 1) void gemm_nt_bf16_kernel(NtArgs g) {
   gemm_tile<GRBW>(g, sm, [&](floatx16 (&acc)[GRBW][2], int i0, int j0, int wm, int wn) {
     const int lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5;
     const int I = g.I, J = g.J;
-    // Lane l holds C[8*(r/4) + 4*hf + r%4][l%32] of each 32x32 block.
+    // Lane l holds C[8*(r/4) + 4*hf + r%4][l%32] of each 32x32 block.  With 16-byte aligned
+    // rows the wave's 128 x 64 block goes through its own 16 KB of the (now idle) LDS stages
+    // in two 64-row halves and leaves as 16-byte stores, 256 contiguous bytes per 16 lanes
+    // (4-byte stores of 32 columns otherwise).  LDS rows are 64 floats with 16-byte chunk c of
+    // row r at c ^ (8 * ((r >> 2) & 1)), so the two lane halves' writes (rows 4 apart) and each
+    // 16 lanes' reads of a row hit distinct banks.
+    const bool vec = (g.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(g.C) & 15) == 0;
+    if (vec) {
+      __syncthreads();  // every wave has read its last fragments from the stages
+      float* st = reinterpret_cast<float*>(&sm) + (threadIdx.x >> 6) * 64 * 64;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = ii * 32 + 8 * (r >> 2) + 4 * hf + (r & 3), col = j * 32 + l32;
+              st[row * 64 + (((col >> 2) ^ (((row >> 2) & 1) << 3)) << 2) + (col & 3)] = acc[2 * half + ii][j][r];
+            }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // LDS in order within the wave
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int row = 4 * k + (lane >> 4), ch = lane & 15;
+          const floatx4 v = *reinterpret_cast<const floatx4*>(st + row * 64 + ((ch ^ (((row >> 2) & 1) << 3)) << 2));
+          const int grow = i0 + wm * 128 + half * 64 + row, gcol = j0 + wn * 64 + 4 * ch;
+          if (grow < I) {
+            float* dst = g.C + static_cast<int64_t>(grow) * g.ldc + gcol;
+            if (gcol + 3 < J) {
+              *reinterpret_cast<floatx4*>(dst) = v;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (gcol + e < J) dst[e] = v[e];
+            }
+          }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next half's writes
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < GRBW; ++i)
 #pragma unroll
