@@ -39,8 +39,10 @@
  * Precision.  IHA_F32: every step in fp32 (the mixing is folded into the
  * weights).  IHA_BF16: the per-head projections run on the bf16 matrix cores
  * with the exact bf16 inputs and fp32 accumulation, the mixing is applied to
- * those fp32 projections in fp32, and the mixed Q/K/V and the attention
- * probabilities are stored as fp16 for the fp16 matrix cores (fp32
+ * those fp32 projections to fp32 accuracy (both operands split into fp16 high
+ * and low parts on the matrix cores, fp32 accumulation, about 2^-21 relative;
+ * shapes without a matrix-core kernel use fp32 FMAs), and the mixed Q/K/V and
+ * the attention probabilities are stored as fp16 for the fp16 matrix cores (fp32
  * accumulation); softmax state, the per-head attention output and X_out are
  * fp32.  Under a causal or window mask the first 32 stacked rows of every
  * (b, h) see the fewest keys and have the largest outputs; their attention is
@@ -254,7 +256,7 @@ iha_status iha_attention_backward(int64_t B, int64_t L, int64_t H, int64_t d, in
  * of iha_forward and iha_attention_backward apply (d = D/H of 64 or 128, P*N stacked
  * rows), and B*N must be at most 2^21 - 64 (IHA_ERR_SHAPE).  workspace: device, 256-byte
  * aligned, at least iha_backward_workspace() bytes, else IHA_ERR_WORKSPACE.
- * Precision: bf16 projections with fp32 accumulation and fp32 mixing, as the forward;
+ * Precision: bf16 projections with fp32 accumulation and fp32-accurate mixing, as the forward;
  * the stacked Q~, K~, V~, dP-bar and the attention's probabilities and dS are fp16
  * matrix-core operands; the reductions over tokens run in fp32; dY enters the dW and dX
  * products as bf16 high and low parts (16 significant bits, fp32 accumulation).
