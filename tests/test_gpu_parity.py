@@ -111,6 +111,11 @@ SMALL = [
     (3, 7, 1280, 20, 1, "window", 3, "bf16"),        # H = 20, R = 7, window inside them
     (1, 77, 1024, 16, 1, "window", 50, "bf16"),      # L = 77: register-copy attention path
     (2, 45, 2560, 20, 2, "causal", None, "bf16"),    # L = 90 (not a multiple of 8), H = 20
+    # the Q~/K~ mixing on the matrix cores: row blocks x k-steps of source heads
+    (1, 256, 2048, 16, 4, "causal", None, "bf16"),   # H*P = 64: two row blocks, one k-step
+    (1, 130, 2048, 32, 4, "window", 50, "bf16"),     # H*P = 128, two k-steps, d = 64
+    (2, 64, 1536, 24, 2, "causal", None, "bf16"),    # H = 24, P = 2: two row blocks, two k-steps
+    (1, 96, 1536, 24, 1, "window", 40, "bf16"),      # H = 24, P = 1: one row block, two k-steps
 ]
 
 
