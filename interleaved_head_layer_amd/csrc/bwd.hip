@@ -26,7 +26,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // fp32 accumulation).  Every operand element is read once.  The waves' tiles are added in LDS
 // in wave order and written as the chunk's partial sums.
 constexpr int kRedCB = 3;               // hj blocks per workgroup
-constexpr int kRedChunkTarget = 512;    // chunks x hj groups is about this (bounds the partials)
+constexpr int kRedChunkTarget = 2048;   // chunks x hj groups is about this (more chunks keep more loads
+                                        // in flight: 512 measured 1.5 % slower, 4096 too; bounds the partials)
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ void split_bf16(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
