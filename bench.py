@@ -441,7 +441,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=64,
                     help="tokens per mode the CPU oracle computes for the headline baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
-    ap.add_argument("--extra-steps", type=int, default=5)
+    ap.add_argument("--extra-steps", type=int, default=5,
+                    help="timed steps of the other workloads (at least 20 forwards, 10 backward calls)")
     ap.add_argument("--only-backward", action="store_true",
                     help="time only the attention backward of the workload's attention shape")
     ap.add_argument("--only-layer-backward", action="store_true",
@@ -526,7 +527,9 @@ def main():
                 continue
             w = wl.WORKLOADS[name]
             f2 = Forwards([w])
-            e = time_steps(f2, args.extra_steps, 5)
+            # Sub-millisecond steps: enough warm-up for the clocks to leave the idle state of
+            # the CPU leg before them, and enough steps to average launch jitter.
+            e = time_steps(f2, max(args.extra_steps, 20), 30)
             roofs = kernel_rooflines(w, e["kms"][0], f2.fused[0])
             dk = max(roofs, key=lambda k: roofs[k]["ms"])
             entry = {"ms_per_step": round(e["ms_step"], 4),
@@ -542,9 +545,9 @@ def main():
                 entry["parity_sample_max_err_over_rms"] = round(s["max_err_over_rms"], 6)
             f2.free()
             extra[name] = entry
-        bwd = run_attention_backward(wl.WORKLOADS[OTHERS[0]], args.extra_steps, 3)
+        bwd = run_attention_backward(wl.WORKLOADS[OTHERS[0]], max(args.extra_steps, 10), 10)
         extra["nexus_inner_causal_b4_l8192_h16"] = run_nexus_inner(4, 8192, 16, 128, "causal",
-                                                                   args.extra_steps, 3)
+                                                                   max(args.extra_steps, 10), 5)
         layer_bwd = {n: run_layer_backward(wl.WORKLOADS[n], args.extra_steps, 2) for n in HEADLINE}
         extra["fused_collapse_ab"] = [run_fused_collapse_ab(wl.WORKLOADS[n], 3)
                                       for n in (OTHERS[0], HEADLINE[0])]
