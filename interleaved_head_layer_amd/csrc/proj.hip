@@ -11,6 +11,8 @@
 //   mix_v   V~^T  [B][H][d][P*N]  fp16
 // The first T0 tokens of every sequence also get fp32 copies (Qe, Ke, Ve) for the
 // full-precision first rows.
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -197,9 +199,12 @@ __device__ __forceinline__ void gemm_tile(const NtArgs& g, NtSmem<RBW>& sm, Epi&
   epi(acc, i0, j0, wm, wn);
 }
 
-static_assert(GWaves * 64 * 64 * sizeof(float) <= sizeof(NtSmem<GRBW>), "epilogue staging");
+// RBW = 4 (256-row tiles) or 5 (320-row tiles: fewer tiles where 256-row tiles would leave
+// the chip's last round of workgroups partly empty).
+template <int RBW>
 __global__ __launch_bounds__(GThreads, 1) void gemm_nt_bf16_kernel(NtArgs g) {
-  __shared__ __attribute__((aligned(16))) NtSmem<GRBW> sm;
+  static_assert(GWaves * 64 * 64 * sizeof(float) <= sizeof(NtSmem<RBW>), "epilogue staging");
+  __shared__ __attribute__((aligned(16))) NtSmem<RBW> sm;
   if (gridDim.y > 1 || gridDim.z > 1) {  // batched launch: product blockIdx.y, K part blockIdx.z
     const int z = blockIdx.y, sp = blockIdx.z;
     g.A += z * g.sa + static_cast<int64_t>(sp) * g.K;
@@ -208,12 +213,13 @@ __global__ __launch_bounds__(GThreads, 1) void gemm_nt_bf16_kernel(NtArgs g) {
     g.C = gridDim.z > 1 ? g.C + (static_cast<int64_t>(sp) * gridDim.y + z) * g.I * g.ldc
                         : z == 0 ? g.Cz[0] : z == 1 ? g.Cz[1] : g.Cz[2];
   }
-  gemm_tile<GRBW>(g, sm, [&](floatx16 (&acc)[GRBW][2], int i0, int j0, int wm, int wn) {
+  gemm_tile<RBW>(g, sm, [&](floatx16 (&acc)[RBW][2], int i0, int j0, int wm, int wn) {
     const int lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5;
     const int I = g.I, J = g.J;
     // Lane l holds C[8*(r/4) + 4*hf + r%4][l%32] of each 32x32 block.  With 16-byte aligned
-    // rows the wave's 128 x 64 block goes through its own 16 KB of the (now idle) LDS stages
-    // in two 64-row halves and leaves as 16-byte stores, 256 contiguous bytes per 16 lanes
+    // rows the wave's (32 RBW) x 64 block goes through its own 16 KB of the (now idle) LDS
+    // stages in pieces of two 32-row blocks (one for an odd last block) and leaves as 16-byte
+    // stores, 256 contiguous bytes per 16 lanes
     // (4-byte stores of 32 columns otherwise).  LDS rows are 64 floats with 16-byte chunk c of
     // row r at c ^ (8 * ((r >> 2) & 1)), so the two lane halves' writes (rows 4 apart) and each
     // 16 lanes' reads of a row hit distinct banks.
@@ -222,9 +228,10 @@ __global__ __launch_bounds__(GThreads, 1) void gemm_nt_bf16_kernel(NtArgs g) {
       __syncthreads();  // every wave has read its last fragments from the stages
       float* st = reinterpret_cast<float*>(&sm) + (threadIdx.x >> 6) * 64 * 64;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
+      for (int half = 0; half < (RBW + 1) / 2; ++half) {
+        const int nb = 2 * half + 1 < RBW ? 2 : 1;  // 32-row blocks in this piece
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii)
+        for (int ii = 0; ii < nb; ++ii)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -234,10 +241,10 @@ __global__ __launch_bounds__(GThreads, 1) void gemm_nt_bf16_kernel(NtArgs g) {
             }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // LDS in order within the wave
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
+        for (int k = 0; k < 8 * nb; ++k) {
           const int row = 4 * k + (lane >> 4), ch = lane & 15;
           const floatx4 v = *reinterpret_cast<const floatx4*>(st + row * 64 + ((ch ^ (((row >> 2) & 1) << 3)) << 2));
-          const int grow = i0 + wm * 128 + half * 64 + row, gcol = j0 + wn * 64 + 4 * ch;
+          const int grow = i0 + wm * 32 * RBW + half * 64 + row, gcol = j0 + wn * 64 + 4 * ch;
           if (grow < I) {
             float* dst = g.C + static_cast<int64_t>(grow) * g.ldc + gcol;
             if (gcol + 3 < J) {
@@ -254,14 +261,14 @@ __global__ __launch_bounds__(GThreads, 1) void gemm_nt_bf16_kernel(NtArgs g) {
       return;
     }
 #pragma unroll
-    for (int i = 0; i < GRBW; ++i)
+    for (int i = 0; i < RBW; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int col = j0 + wn * 64 + j * 32 + l32;
         if (col >= J) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = i0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const int row = i0 + wm * 32 * RBW + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
           if (row < I) g.C[static_cast<int64_t>(row) * g.ldc + col] = acc[i][j][r];
         }
       }
@@ -492,11 +499,35 @@ __global__ __launch_bounds__(GThreads, 1) void gemm_mix_bf16_kernel(NtArgs g, Pr
   });
 }
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 // Launch C = A B^T, splitting A's rows or B's rows into chunks whose bytes fit the 32-bit
-// buffer offsets (a chunk is a multiple of the tile height).
+// buffer offsets (a chunk is a multiple of the tile height).  One workgroup fills a CU, so
+// the launch runs in rounds of (CU count) tiles; 320-row tiles are taken when their rounds
+// cover fewer rows per CU than 256-row tiles' (e.g. 2560 x 16384: 512 tiles in 2 rounds of
+// 320 rows against 640 tiles in 3 rounds of 256 on 256 CUs).
 hipError_t launch_gemm_nt(NtArgs g, hipStream_t s) {
   const int64_t max_rows = ((int64_t{1} << 31) - 1) / (static_cast<int64_t>(g.K) * 2) / GTI * GTI;
   if (max_rows < GTI) return hipErrorInvalidValue;
+  if (g.I <= max_rows && g.J <= max_rows) {
+    const int64_t cus = device_cus(), ntj = (g.J + GTJ - 1) / GTJ;
+    const int64_t t4 = (g.I + 255) / 256 * ntj, t5 = (g.I + 319) / 320 * ntj;
+    if ((t5 + cus - 1) / cus * 320 < (t4 + cus - 1) / cus * 256) {
+      hipLaunchKernelGGL(gemm_nt_bf16_kernel<5>, dim3(static_cast<unsigned>(t5)), dim3(GThreads), 0, s, g);
+      return hipGetLastError();
+    }
+  }
   const NtArgs full = g;
   for (int64_t i0 = 0; i0 < full.I; i0 += max_rows) {
     for (int64_t j0 = 0; j0 < full.J; j0 += max_rows) {
@@ -507,7 +538,7 @@ hipError_t launch_gemm_nt(NtArgs g, hipStream_t s) {
       c.I = static_cast<int>(std::min<int64_t>(max_rows, full.I - i0));
       c.J = static_cast<int>(std::min<int64_t>(max_rows, full.J - j0));
       const int tiles = ((c.I + GTI - 1) / GTI) * ((c.J + GTJ - 1) / GTJ);
-      hipLaunchKernelGGL(gemm_nt_bf16_kernel, dim3(tiles), dim3(GThreads), 0, s, c);
+      hipLaunchKernelGGL(gemm_nt_bf16_kernel<GRBW>, dim3(tiles), dim3(GThreads), 0, s, c);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -1026,7 +1057,7 @@ hipError_t launch_gemm_nt_splitk(const NtArgs& g, int batch, int splits, float* 
   const int64_t max_rows = ((int64_t{1} << 31) - 1) / (static_cast<int64_t>(c.ks) * 2) / GTI * GTI;
   if (max_rows < g.I || max_rows < g.J) return hipErrorInvalidValue;
   const int tiles = ((g.I + GTI - 1) / GTI) * ((g.J + GTJ - 1) / GTJ);
-  hipLaunchKernelGGL(gemm_nt_bf16_kernel, dim3(tiles, batch, splits), dim3(GThreads), 0, s, c);
+  hipLaunchKernelGGL(gemm_nt_bf16_kernel<GRBW>, dim3(tiles, batch, splits), dim3(GThreads), 0, s, c);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n = static_cast<int64_t>(g.I) * g.ldc;
@@ -1050,7 +1081,7 @@ hipError_t launch_gemm_nt_batched(const NtArgs& g, int batch, hipStream_t s) {
     return hipSuccess;
   }
   const int tiles = ((g.I + GTI - 1) / GTI) * ((g.J + GTJ - 1) / GTJ);
-  hipLaunchKernelGGL(gemm_nt_bf16_kernel, dim3(tiles, batch), dim3(GThreads), 0, s, g);
+  hipLaunchKernelGGL(gemm_nt_bf16_kernel<GRBW>, dim3(tiles, batch), dim3(GThreads), 0, s, g);
   return hipGetLastError();
 }
 

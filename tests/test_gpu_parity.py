@@ -179,6 +179,21 @@ def test_full_size_wide_causal_sampled(progress):
     check(gpu[tokens], ref, BF16_TOL, rms=rms, what=f"{w.name} ({len(tokens)} tokens)")
 
 
+@pytest.mark.timeout(600)
+def test_unfused_projection_320_row_tiles(progress):
+    """An unfused shape (24 heads) sized so that on a 256-CU device both projection GEMMs
+    take 320-row tiles (fewer rounds of workgroups than 256-row tiles): Y_QK is 5632 x 6144
+    (18 row tiles, the last 192 of 320 rows) and Y_V^T 3072 x 5632 (10 row tiles, the last
+    192 rows).  Every output element against the oracle."""
+    w = wl.custom(1, 5632, 3072, 24, 1, "window", seed=5632, window=256)
+    note(w.describe())
+    x = wl.make_inputs(w)
+    gpu = gpu_forward(w, x)
+    progress(f"{w.name}: oracle on all {w.B * w.N} tokens ({oracle.threads()} threads)")
+    ref = oracle_forward(w, x)
+    check(gpu, ref, BF16_TOL, what=f"{w.name} (whole output)")
+
+
 @pytest.mark.parametrize("scale", [2.0, 4.0])
 def test_peaked_softmax_rows(scale):
     """X scaled up (scores about scale^2 larger: nearly one-hot softmax rows, many offset
