@@ -77,19 +77,21 @@ static_assert(GK == 64, "the main loop walks four k-steps of 16 per slice");
 
 __device__ __forceinline__ int gswz(int r) { return (r >> 1) & 7; }
 
-template <int RBW>
+template <int RBW, int NW = GWaves>
 struct NtSmem {
   uint16_t a[2][64 * RBW * GK];
-  uint16_t b[2][GTJ * GK];
+  uint16_t b[2][32 * NW * GK];
 };
 
-// Main loop of one (64 RBW) x 256 tile; hands the accumulators to epi(acc, i0, j0, wm, wn).
-template <int RBW, typename Epi>
-__device__ __forceinline__ void gemm_tile(const NtArgs& g, NtSmem<RBW>& sm, Epi&& epi) {
-  constexpr int TI = 64 * RBW;
+// Main loop of one (64 RBW) x (32 NW) tile of NW waves (2 x NW/2, each (32 RBW) x 64; NW = 8,
+// or 4 for grids too small to give every CU a tile); hands the accumulators to
+// epi(acc, i0, j0, wm, wn).
+template <int RBW, int NW = GWaves, typename Epi>
+__device__ __forceinline__ void gemm_tile(const NtArgs& g, NtSmem<RBW, NW>& sm, Epi&& epi) {
+  constexpr int TI = 64 * RBW, TJ = 32 * NW;
   const int I = g.I, J = g.J, K = g.K;
   const int64_t KS = g.ks > 0 ? g.ks : K;  // row stride of A and B
-  const int ntj = (J + GTJ - 1) / GTJ, nti = (I + TI - 1) / TI;
+  const int ntj = (J + TJ - 1) / TJ, nti = (I + TI - 1) / TI;
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   // Groups of 4 row tiles sweep the column tiles, so a group's A slices stay in L2.
   constexpr int GR = 4;
@@ -98,32 +100,32 @@ __device__ __forceinline__ void gemm_tile(const NtArgs& g, NtSmem<RBW>& sm, Epi&
   const int gsize = min(GR, nti - first_i);
   const int ti = first_i + (lid % (GR * ntj)) % gsize;
   const int tj = (lid % (GR * ntj)) / gsize;
-  const int i0 = ti * TI, j0 = tj * GTJ;
+  const int i0 = ti * TI, j0 = tj * TJ;
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / (NW / 2), wn = wave % (NW / 2);
 
   // Readable bytes end with the last valid row's K values: rows past I / J read zero.
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(g.A), static_cast<short>(0), static_cast<int>(((I - 1) * KS + K) * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(g.B), static_cast<short>(0), static_cast<int>(((J - 1) * KS + K) * 2), 0x00020000);
-  // Copy slot (p * 8 + wave) * 64 + lane of a stage -> row 64p + 8 * wave + lane / 8, chunk
-  // lane % 8; the swizzle depends on the row only through 8 * wave + lane / 8.
+  // Copy slot (p * NW + wave) * 64 + lane of a stage -> row 8 NW p + 8 * wave + lane / 8,
+  // chunk lane % 8; the swizzle depends on the row only through 8 * wave + lane / 8.
   const int rl = 8 * wave + (lane >> 3), pos = lane & 7;
   const unsigned loff = static_cast<unsigned>((rl * KS + (pos ^ gswz(rl)) * 8) * 2);
   auto issue = [&](int k0, int st) {
 #pragma unroll
-    for (int p = 0; p < TI / 64; ++p)
+    for (int p = 0; p < TI / (8 * NW); ++p)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (__attribute__((address_space(3))) void*)(sm.a[st] + (p * GWaves + wave) * 512), 16, loff,
-          static_cast<unsigned>((static_cast<int64_t>(i0 + 64 * p) * KS + k0) * 2), 0, 0);
+          ra, (__attribute__((address_space(3))) void*)(sm.a[st] + (p * NW + wave) * 512), 16, loff,
+          static_cast<unsigned>((static_cast<int64_t>(i0 + 8 * NW * p) * KS + k0) * 2), 0, 0);
 #pragma unroll
-    for (int p = 0; p < GTJ / 64; ++p)
+    for (int p = 0; p < TJ / (8 * NW); ++p)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rb, (__attribute__((address_space(3))) void*)(sm.b[st] + (p * GWaves + wave) * 512), 16, loff,
-          static_cast<unsigned>((static_cast<int64_t>(j0 + 64 * p) * KS + k0) * 2), 0, 0);
+          rb, (__attribute__((address_space(3))) void*)(sm.b[st] + (p * NW + wave) * 512), 16, loff,
+          static_cast<unsigned>((static_cast<int64_t>(j0 + 8 * NW * p) * KS + k0) * 2), 0, 0);
   };
 
   // Per-lane LDS element offsets of the A / B fragments; k-step s reads chunk 2s + hf.
@@ -347,11 +349,11 @@ __device__ __forceinline__ floatx16 mix_channel(const half8 (&yh)[RBW][2], const
   return o;
 }
 
-template <int H, int P>
-__global__ __launch_bounds__(GThreads, 1) void gemm_mix_bf16_kernel(NtArgs g, ProjArgs pa) {
+template <int H, int P, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_mix_bf16_kernel(NtArgs g, ProjArgs pa) {
   constexpr int RBW = H / 4, HP = H * P, MB = (HP + 31) / 32;
-  __shared__ __attribute__((aligned(16))) NtSmem<RBW> sm;
-  gemm_tile<RBW>(g, sm, [&](floatx16 (&acc)[RBW][2], int i0, int j0, int wm, int wn) {
+  __shared__ __attribute__((aligned(16))) NtSmem<RBW, NW> sm;
+  gemm_tile<RBW, NW>(g, sm, [&](floatx16 (&acc)[RBW][2], int i0, int j0, int wm, int wn) {
     const int lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5;
     const int D = pa.D, d = pa.d, N = pa.N, M = pa.B * pa.N;
     const int which = i0 / D;                          // tiles never straddle Q / K / V
@@ -370,7 +372,7 @@ __global__ __launch_bounds__(GThreads, 1) void gemm_mix_bf16_kernel(NtArgs g, Pr
       return row < HP ? al[m * HP + row] : 0.f;
     };
     if constexpr (kLdsAlpha) {
-      for (int x = threadIdx.x; x < 2 * MB * 64; x += GThreads) {  // (rest?, mb, lane)
+      for (int x = threadIdx.x; x < 2 * MB * 64; x += NW * 64) {  // (rest?, mb, lane)
         const int ln = x & 63, mb = (x >> 6) % MB, kind = 2 * (x / (64 * MB));
         const int row = mb * 32 + (ln & 31), hfx = ln >> 5;
         half8 vh, vl;
@@ -1161,13 +1163,21 @@ hipError_t launch_proj_bf16(const ProjArgs& pa, hipStream_t s, hipEvent_t ev_pre
       c.B = pa.X + jb * D;
       c.J = static_cast<int>(std::min<int64_t>(max_j, M - jb));
       c.jbase = static_cast<int>(jb);
-      const int64_t tiles = static_cast<int64_t>(3 * D / ti) * ((c.J + GTJ - 1) / GTJ);
-      const int key = pa.H * 8 + pa.P;
+      // 8-wave 256-token tiles; 4-wave 128-token tiles where the former would leave CUs
+      // without a tile (one workgroup per CU: twice the tiles at one wave per SIMD).
+      const int64_t tiles8 = static_cast<int64_t>(3 * D / ti) * ((c.J + GTJ - 1) / GTJ);
+      const bool small = tiles8 < device_cus();
+      const int64_t tiles = small ? static_cast<int64_t>(3 * D / ti) * ((c.J + 127) / 128) : tiles8;
+      const int key = (pa.H * 8 + pa.P) * 2 + (small ? 1 : 0);
       switch (key) {
-        case 16 * 8 + 1: hipLaunchKernelGGL((gemm_mix_bf16_kernel<16, 1>), dim3(tiles), dim3(GThreads), 0, s, c, pa); break;
-        case 16 * 8 + 2: hipLaunchKernelGGL((gemm_mix_bf16_kernel<16, 2>), dim3(tiles), dim3(GThreads), 0, s, c, pa); break;
-        case 20 * 8 + 1: hipLaunchKernelGGL((gemm_mix_bf16_kernel<20, 1>), dim3(tiles), dim3(GThreads), 0, s, c, pa); break;
-        case 20 * 8 + 2: hipLaunchKernelGGL((gemm_mix_bf16_kernel<20, 2>), dim3(tiles), dim3(GThreads), 0, s, c, pa); break;
+        case (16 * 8 + 1) * 2: hipLaunchKernelGGL((gemm_mix_bf16_kernel<16, 1, 8>), dim3(tiles), dim3(512), 0, s, c, pa); break;
+        case (16 * 8 + 2) * 2: hipLaunchKernelGGL((gemm_mix_bf16_kernel<16, 2, 8>), dim3(tiles), dim3(512), 0, s, c, pa); break;
+        case (20 * 8 + 1) * 2: hipLaunchKernelGGL((gemm_mix_bf16_kernel<20, 1, 8>), dim3(tiles), dim3(512), 0, s, c, pa); break;
+        case (20 * 8 + 2) * 2: hipLaunchKernelGGL((gemm_mix_bf16_kernel<20, 2, 8>), dim3(tiles), dim3(512), 0, s, c, pa); break;
+        case (16 * 8 + 1) * 2 + 1: hipLaunchKernelGGL((gemm_mix_bf16_kernel<16, 1, 4>), dim3(tiles), dim3(256), 0, s, c, pa); break;
+        case (16 * 8 + 2) * 2 + 1: hipLaunchKernelGGL((gemm_mix_bf16_kernel<16, 2, 4>), dim3(tiles), dim3(256), 0, s, c, pa); break;
+        case (20 * 8 + 1) * 2 + 1: hipLaunchKernelGGL((gemm_mix_bf16_kernel<20, 1, 4>), dim3(tiles), dim3(256), 0, s, c, pa); break;
+        case (20 * 8 + 2) * 2 + 1: hipLaunchKernelGGL((gemm_mix_bf16_kernel<20, 2, 4>), dim3(tiles), dim3(256), 0, s, c, pa); break;
         default: return hipErrorInvalidValue;
       }
       if ((e = hipGetLastError()) != hipSuccess) return e;
