@@ -63,8 +63,9 @@ __global__ __launch_bounds__(256) void wprep_kernel(ProjArgs pa, int cm) {
 // ------------------------------------------------------------------- NT GEMM
 // C[i][j] = sum_k A[i][k] * B[j][k]; A [I][K], B [J][K] bf16 (k contiguous), C fp32 with
 // row stride ldc; K a multiple of 64.  TI x 256 tiles (TI = 64 RBW: 256, or 320 for the
-// fused mixing with 20 heads), 8 waves as 2 x 4 (32 RBW x 64 each: every A fragment read
-// from LDS feeds two matrix-core products, every B fragment RBW),
+// fused mixing with 20 heads and for plain products that need fewer workgroup rounds so),
+// 8 waves as 2 x 4 (32 RBW x 64 each: every A fragment read from LDS feeds two matrix-core
+// products, every B fragment RBW; small fused grids take 4 waves and 128-column tiles),
 // K slices of 64 in a two-stage LDS ring filled by buffer loads straight into LDS, register
 // fragments read one k-step ahead of the products that use them.  Rows
 // are 128 bytes with 16-byte chunks XOR-swizzled by (row >> 1) & 7, so the 16 lanes that
